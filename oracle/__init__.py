@@ -1,0 +1,7 @@
+"""Float64 CPU oracle (test infrastructure only; see ``oracle.attention``)."""
+
+from .attention import (combine, decode, decode_keys, default_kv_map, prefill, prefill_rows,
+                        sink_attention, split_partials, visible)
+
+__all__ = ["combine", "decode", "decode_keys", "default_kv_map", "prefill", "prefill_rows",
+           "sink_attention", "split_partials", "visible"]

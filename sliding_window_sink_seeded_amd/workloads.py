@@ -1,0 +1,108 @@
+"""The five measured workloads and their algorithmic work.
+
+Shapes follow the MiMo-V2-Flash Technical Report review (xllm-io), §3.1: window 128; 64 query heads
+over 8 KV heads for sliding-window layers and over 4 KV heads for global layers; Q/K head dim 192,
+V head dim 128. Decode carries 1 + 3 draft tokens per sequence (same page, §2: three MTP layers used
+as the self-speculative draft), and the global decode runs at the 256K context of the same page §1.
+
+Algorithmic work counts only what the method must do:
+* FLOPs: 2 * (dqk + dv) per visible (query, key) score; nothing masked or skipped is counted.
+* Bytes: Q read once, the union of visible K/V read once, new K/V read once, O written once.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str  # "prefill" or "decode"
+    dtype: str  # "f32" or "bf16"
+    Hq: int
+    Hkv: int
+    window: int
+    dqk: int = 192
+    dv: int = 128
+    B: int = 1
+    L: int = 0  # prefill sequence length
+    T: int = 0  # decode: new tokens per sequence
+    C: int = 0  # decode: cache slots per sequence
+    P: int = 0  # decode: fixed committed length (0 -> drawn from len_range)
+    len_range: tuple = ()  # decode: committed lengths uniform on [lo, hi)
+    ring_offsets: bool = False
+    seed: int = 0
+    description: str = ""
+
+    @property
+    def elem(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.dqk)
+
+
+WORKLOADS = {
+    "swa_prefill_f32": Workload(
+        "swa_prefill_f32", "prefill", "f32", 64, 8, 128, B=1, L=512, seed=1,
+        description="sliding-window prefill fp32, batch 1 x 512, 64/8 heads, W=128"),
+    "swa_prefill_bf16": Workload(
+        "swa_prefill_bf16", "prefill", "bf16", 64, 8, 128, B=4, L=32768, seed=2,
+        description="sliding-window prefill bf16, batch 4 x 32768, 64/8 heads, W=128"),
+    "ga_prefill_bf16": Workload(
+        "ga_prefill_bf16", "prefill", "bf16", 64, 4, 32768, B=1, L=32768, seed=3,
+        description="global causal prefill bf16, batch 1 x 32768, 64/4 heads"),
+    "swa_decode_bf16": Workload(
+        "swa_decode_bf16", "decode", "bf16", 64, 8, 128, B=256, T=4, C=128,
+        len_range=(128, 32768), ring_offsets=True, seed=4,
+        description="sliding-window decode bf16, 256 seqs x 4 tokens, 128-slot ring, 64/8 heads"),
+    "ga_decode_bf16": Workload(
+        "ga_decode_bf16", "decode", "bf16", 64, 4, 1 << 30, B=8, T=4, C=262144, P=262144, seed=5,
+        description="global decode bf16, 8 seqs x 262144 cached + 4 tokens, 64/4 heads, split-KV"),
+}
+
+
+def prefill_scores(B: int, L: int, Hq: int, window: int) -> int:
+    """Visible (query, key) pairs of a prefill: row i sees min(i + 1, W) keys."""
+    w = min(window, L)
+    per_head = w * (w + 1) // 2 + (L - w) * w
+    return B * Hq * per_head
+
+
+def prefill_bytes(w: Workload) -> int:
+    e = w.elem
+    q = w.B * w.L * w.Hq * w.dqk * e
+    kv = w.B * w.L * w.Hkv * (w.dqk + w.dv) * e
+    o = w.B * w.L * w.Hq * w.dv * e
+    return q + kv + o
+
+
+def decode_scores(lens: np.ndarray, T: int, Hq: int, window: int) -> int:
+    total = 0
+    for P in np.asarray(lens, dtype=np.int64):
+        for t in range(T):
+            total += min(int(P) + t + 1, window)
+    return int(total * Hq)
+
+
+def decode_bytes(w: Workload, lens: np.ndarray) -> int:
+    e = w.elem
+    committed = sum(min(int(P), w.window - 1) for P in np.asarray(lens, dtype=np.int64))
+    q = w.B * w.T * w.Hq * w.dqk * e
+    cache = committed * w.Hkv * (w.dqk + w.dv) * e
+    new = w.B * w.T * w.Hkv * (w.dqk + w.dv) * e
+    o = w.B * w.T * w.Hq * w.dv * e
+    return q + cache + new + o
+
+
+def algorithmic(w: Workload, lens: np.ndarray | None = None) -> tuple[int, int]:
+    """(FLOPs, bytes) of one pass over workload ``w`` (decode needs the drawn lengths)."""
+    per_score = 2 * (w.dqk + w.dv)
+    if w.kind == "prefill":
+        return prefill_scores(w.B, w.L, w.Hq, w.window) * per_score, prefill_bytes(w)
+    return decode_scores(lens, w.T, w.Hq, w.window) * per_score, decode_bytes(w, lens)
