@@ -1,0 +1,125 @@
+/*
+ * mimo_attn.h - C ABI of the MI355X (gfx950) sink-seeded sliding-window / global attention library.
+ *
+ * The operation (MiMo-V2-Flash Technical Report review (xllm-io), §3.1-§3.2; MiMo series notes
+ * (plmsmile), MiMo-V2-Flash > local window and > Learnable Attention Sink > mechanism):
+ * for batch b, query head h (KV head g = map(h)) and query position i,
+ *
+ *     s_ij  = scale * <q[b,i,h,:], k[b,j,g,:]>            for visible keys j
+ *     o[b,i,h,:] = sum_j exp(s_ij) v[b,j,g,:] / (exp(sink[h]) + sum_j exp(s_ij))
+ *     lse   = log(exp(sink[h]) + sum_j exp(s_ij))           (natural log, sink included)
+ *
+ * Key j is visible to query i iff 0 <= i - j < window (the window counts the query's own key);
+ * window >= sequence length gives plain causal (global) attention. The sink is a per-query-head
+ * logit that enters only the denominator: it is not multiplied by `scale` and carries no value, so
+ * the weights of the real keys sum to less than one. A NULL sink pointer means "no sink".
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, row-major, last dimension contiguous, and 16-byte aligned.
+ *  - Every pointer except `kv_head_of_q` is a DEVICE pointer owned by the caller. The library
+ *    allocates nothing, frees nothing, keeps no state besides a thread-local error string, and
+ *    never synchronises: work is enqueued on `stream` and the call returns.
+ *  - All arguments are validated on the host before anything is launched. On a non-zero return
+ *    nothing has been launched and no output has been written; mimo_attn_last_error() explains.
+ *  - Device faults are asynchronous and surface at the caller's next synchronisation.
+ *  - Results are deterministic: fixed reduction order, no atomics.
+ *  - The library is reentrant; calls that write the same outputs or workspace race.
+ *  - Sink entries may be finite or -inf; +inf or NaN sink entries give undefined results.
+ *  - Supported head dims: d_qk = 192, d_v = 128 (the MiMo-V2-Flash shapes); anything else returns
+ *    MIMO_EUNSUPPORTED.
+ */
+#ifndef MIMO_ATTN_H
+#define MIMO_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage dtype shared by q, k, v, the caches and o. Softmax and accumulation are fp32 for both. */
+typedef enum { MIMO_F32 = 0, MIMO_BF16 = 1 } mimo_dtype;
+
+enum {
+  MIMO_OK = 0,
+  MIMO_EINVAL = -1,      /* a size, pointer, alignment, head map or window argument is invalid */
+  MIMO_EUNSUPPORTED = -2, /* valid request that this build does not implement (dtype/dims)       */
+  MIMO_EWORKSPACE = -3,  /* decode workspace missing or smaller than the size query returned     */
+  MIMO_EHIP = -4         /* the HIP runtime refused a launch                                      */
+};
+
+/*
+ * Prefill: every query position of every sequence attends to its window of keys.
+ *
+ *   q     [B, L, Hq,  d_qk]  dtype dt        k [B, L, Hkv, d_qk]   v [B, L, Hkv, d_v]
+ *   o     [B, L, Hq,  d_v]   dtype dt        (written)
+ *   lse   [B, Hq, L] fp32, nullable          (written when non-NULL)
+ *   sink  [Hq] fp32 device, nullable (NULL = no sink, same as every entry -inf)
+ *   kv_head_of_q [Hq] int32 HOST array, nullable. NULL means h / (Hq/Hkv). Otherwise every KV head
+ *         must serve exactly Hq/Hkv query heads; query heads of one KV head are processed together.
+ *   window >= 1; window >= L selects global causal attention. scale multiplies q.k only.
+ *
+ * Errors: MIMO_EINVAL for B, L, Hq, Hkv < 1, Hq % Hkv != 0, a bad head map, window < 1, NULL or
+ * misaligned q/k/v/o, misaligned sink/lse, non-finite scale, or tensors larger than 2^62 bytes;
+ * MIMO_EUNSUPPORTED for other head dims or dtypes; MIMO_EHIP if the launch fails.
+ */
+int mimo_attn_prefill(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v,
+                      const void* q, const void* k, const void* v, int window, const float* sink,
+                      const int32_t* kv_head_of_q, float scale, void* o, float* lse,
+                      hipStream_t stream);
+
+/*
+ * Bytes of device workspace that mimo_attn_decode needs for the same arguments (0 when the
+ * single-pass path is used). num_splits follows mimo_attn_decode: 0 = automatic choice.
+ * Returns 0 for arguments mimo_attn_decode would reject.
+ */
+size_t mimo_attn_decode_workspace_size(int B, int T, int Hq, int Hkv, int d_v, int max_cache_len,
+                                       int window, int num_splits);
+
+/*
+ * Decode / MTP verification: T new tokens per sequence (the next token plus up to three drafts,
+ * MiMo series notes, MiMo-V2-Flash > lightweight MTP > inference), attending to committed cache
+ * entries and, causally, to each other.
+ *
+ *   q       [B, T, Hq,  d_qk]            k_new [B, T, Hkv, d_qk]   v_new [B, T, Hkv, d_v]
+ *   k_cache [B, C, Hkv, d_qk]            v_cache [B, C, Hkv, d_v]
+ *   cache_len    [B] int32 device: committed tokens P_b (new tokens excluded), 0 <= P_b <= max_cache_len.
+ *   cache_offset [B] int32 device, nullable (NULL = 0): committed position p of sequence b is stored
+ *                in slot (p + cache_offset[b]) mod C. A sliding-window layer uses a ring of
+ *                C >= window - 1 slots; a global layer uses a linear cache with C >= max_cache_len.
+ *   New token t sits at position P_b + t and sees committed positions >= P_b + t - window + 1 and new
+ *   tokens 0..t. The caller appends accepted tokens to the cache afterwards.
+ *   o   [B, T, Hq, d_v] dtype dt (written);  lse [B, T, Hq] fp32, nullable.
+ *   num_splits: 0 = automatic; 1 = single pass per (sequence, KV head); > 1 = split the visible keys
+ *   into that many chunks (partials in `workspace`) followed by a combine that adds the sink once.
+ *   workspace / workspace_bytes: device scratch of at least mimo_attn_decode_workspace_size(...)
+ *   bytes (may be NULL when that size is 0). Its contents are overwritten.
+ *
+ * Errors: MIMO_EINVAL for sizes < 1, T outside 1..4, Hq % Hkv != 0, a bad head map, window < 1,
+ * max_cache_len < 0, a cache too small for the window (C < min(window - 1, max_cache_len)),
+ * num_splits < 0, NULL or misaligned pointers; MIMO_EWORKSPACE when the workspace is too small;
+ * MIMO_EUNSUPPORTED for other head dims or dtypes; MIMO_EHIP if a launch fails.
+ * cache_len entries outside [0, max_cache_len] are clamped into that range on the device.
+ */
+int mimo_attn_decode(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
+                     const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                     const void* v_cache, int C, const int32_t* cache_len,
+                     const int32_t* cache_offset, int max_cache_len, int window,
+                     const float* sink, const int32_t* kv_head_of_q, float scale, int num_splits,
+                     void* workspace, size_t workspace_bytes, void* o, float* lse,
+                     hipStream_t stream);
+
+/* Thread-local description of the last non-zero return on this thread ("" if none). */
+const char* mimo_attn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int mimo_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIMO_ATTN_H */

@@ -1,0 +1,212 @@
+"""MI355X (gfx950) sink-seeded sliding-window / global attention: Python binding of libmimo_attn.
+
+The binding only marshals arguments to the C ABI (include/mimo_attn.h): it checks tensor
+placement, dtype and shape, allocates outputs when none are given, and passes raw device pointers
+plus the current HIP stream. Every step of the computation runs in the HIP kernels; there is no
+fallback. If the shared library is missing, every call raises.
+
+    o, lse = prefill(q, k, v, window=128, sink=sink)          # q [B, L, Hq, 192] ...
+    o, lse = decode(q, k_new, v_new, k_cache, v_cache, cache_len, window=128, ...)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["prefill", "decode", "decode_workspace_size", "last_error", "version", "library",
+           "LIB_PATH", "MimoError", "EXPORTS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmimo_attn.so")
+EXPORTS = ("mimo_attn_prefill", "mimo_attn_decode", "mimo_attn_decode_workspace_size",
+           "mimo_attn_last_error", "mimo_attn_version")
+
+MIMO_F32, MIMO_BF16 = 0, 1
+_CODES = {-1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP"}
+
+
+class MimoError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mimo_attn {_CODES.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Loads libmimo_attn.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.mimo_attn_prefill.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp,
+                                      f32, vp, vp, vp]
+    lib.mimo_attn_prefill.restype = i32
+    lib.mimo_attn_decode_workspace_size.argtypes = [i32] * 8
+    lib.mimo_attn_decode_workspace_size.restype = sz
+    lib.mimo_attn_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp,
+                                     vp, i32, i32, vp, vp, f32, i32, vp, sz, vp, vp, vp]
+    lib.mimo_attn_decode.restype = i32
+    lib.mimo_attn_last_error.argtypes = []
+    lib.mimo_attn_last_error.restype = ctypes.c_char_p
+    lib.mimo_attn_version.argtypes = []
+    lib.mimo_attn_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return library().mimo_attn_last_error().decode()
+
+
+def version() -> int:
+    return library().mimo_attn_version()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise MimoError(rc, last_error())
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return MIMO_BF16
+    if t.dtype == torch.float32:
+        return MIMO_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _kv_map(kv_map, Hq):
+    if kv_map is None:
+        return None, None
+    arr = (ctypes.c_int32 * Hq)(*[int(x) for x in kv_map])
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def prefill(q, k, v, window: int, sink=None, scale: float | None = None, kv_map=None, out=None,
+            lse=None, return_lse: bool = False, stream=None):
+    """Sink-seeded windowed prefill. q [B, L, Hq, dqk], k [B, L, Hkv, dqk], v [B, L, Hkv, dv].
+
+    window >= L means global causal attention. sink: fp32 [Hq] GPU tensor or None. kv_map: host
+    sequence of Hq KV-head indices (None = contiguous groups). Returns (o, lse or None).
+    """
+    import torch
+
+    _dev(q, "q", ndim=4)
+    dt = _dtype_code(q)
+    _dev(k, "k", q.dtype, 4)
+    _dev(v, "v", q.dtype, 4)
+    B, L, Hq, dqk = q.shape
+    Hkv, dv = k.shape[2], v.shape[3]
+    if tuple(k.shape[:2]) != (B, L) or tuple(v.shape[:3]) != (B, L, Hkv) or k.shape[3] != dqk:
+        raise ValueError("q, k, v shapes disagree")
+    if sink is not None:
+        _dev(sink, "sink", torch.float32, 1)
+        if sink.shape[0] != Hq:
+            raise ValueError("sink must have Hq entries")
+    if out is None:
+        out = torch.empty((B, L, Hq, dv), dtype=q.dtype, device=q.device)
+    _dev(out, "out", q.dtype, 4)
+    if tuple(out.shape) != (B, L, Hq, dv):
+        raise ValueError("out has the wrong shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, Hq, L):
+            raise ValueError("lse has the wrong shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    keep, kvm = _kv_map(kv_map, Hq)
+    rc = library().mimo_attn_prefill(dt, B, L, Hq, Hkv, dqk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                     int(window), _ptr(sink), kvm, float(scale), _ptr(out),
+                                     _ptr(lse), _stream(stream))
+    del keep
+    _check(rc)
+    return out, lse
+
+
+def decode_workspace_size(B, T, Hq, Hkv, dv, max_cache_len, window, num_splits=0) -> int:
+    return int(library().mimo_attn_decode_workspace_size(B, T, Hq, Hkv, dv, max_cache_len, window,
+                                                         num_splits))
+
+
+def decode(q, k_new, v_new, k_cache, v_cache, cache_len, window: int, max_cache_len: int,
+           cache_offset=None, sink=None, scale: float | None = None, kv_map=None,
+           num_splits: int = 0, workspace=None, out=None, lse=None, return_lse: bool = False,
+           stream=None):
+    """Decode / MTP verify of T = q.shape[1] new tokens per sequence.
+
+    q [B, T, Hq, dqk]; k_new/v_new [B, T, Hkv, d]; k_cache/v_cache [B, C, Hkv, d];
+    cache_len / cache_offset int32 [B] GPU tensors. Returns (o, lse or None).
+    """
+    import torch
+
+    _dev(q, "q", ndim=4)
+    dt = _dtype_code(q)
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(t, name, q.dtype, 4)
+    B, T, Hq, dqk = q.shape
+    Hkv, dv, C = k_new.shape[2], v_new.shape[3], k_cache.shape[1]
+    if (tuple(k_new.shape) != (B, T, Hkv, dqk) or tuple(v_new.shape[:3]) != (B, T, Hkv)
+            or tuple(k_cache.shape) != (B, C, Hkv, dqk) or tuple(v_cache.shape) != (B, C, Hkv, dv)):
+        raise ValueError("decode tensor shapes disagree")
+    _dev(cache_len, "cache_len", torch.int32, 1)
+    if cache_offset is not None:
+        _dev(cache_offset, "cache_offset", torch.int32, 1)
+    if sink is not None:
+        _dev(sink, "sink", torch.float32, 1)
+    if out is None:
+        out = torch.empty((B, T, Hq, dv), dtype=q.dtype, device=q.device)
+    _dev(out, "out", q.dtype, 4)
+    if lse is None and return_lse:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, 3)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    ws_bytes = decode_workspace_size(B, T, Hq, Hkv, dv, max_cache_len, window, num_splits)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    keep, kvm = _kv_map(kv_map, Hq)
+    rc = library().mimo_attn_decode(dt, B, T, Hq, Hkv, dqk, dv, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                    _ptr(k_cache), _ptr(v_cache), C, _ptr(cache_len),
+                                    _ptr(cache_offset), int(max_cache_len), int(window), _ptr(sink),
+                                    kvm, float(scale), int(num_splits), _ptr(workspace), ws_have,
+                                    _ptr(out), _ptr(lse), _stream(stream))
+    del keep
+    _check(rc)
+    return out, lse

@@ -1,0 +1,201 @@
+// Host side of the C ABI declared in include/mimo_attn.h: argument validation, head grouping,
+// decode split planning and kernel launches on the caller's stream. Nothing here allocates,
+// frees or synchronises.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/mimo_attn.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Builds the query-head list grouped by KV head; returns 0 or an error code.
+int group_heads(int Hq, int Hkv, const int32_t* kv_head_of_q, mimo::HeadList* hl) {
+  const int G = Hq / Hkv;
+  if (!kv_head_of_q) {
+    for (int h = 0; h < Hq; ++h) hl->heads[h] = (int16_t)h;
+    return MIMO_OK;
+  }
+  int fill[mimo::kMaxHeads] = {0};
+  for (int h = 0; h < Hq; ++h) {
+    const int g = kv_head_of_q[h];
+    if (g < 0 || g >= Hkv) return fail(MIMO_EINVAL, "kv_head_of_q[%d] = %d is outside [0, %d)", h, g, Hkv);
+    if (fill[g] >= G) return fail(MIMO_EINVAL, "KV head %d serves more than Hq/Hkv = %d query heads", g, G);
+    hl->heads[g * G + fill[g]++] = (int16_t)h;
+  }
+  return MIMO_OK;  // every KV head now has exactly G heads (counts sum to Hq)
+}
+
+int check_common(int dt, int B, int Hq, int Hkv, int d_qk, int d_v, int window, float scale) {
+  if (dt != MIMO_F32 && dt != MIMO_BF16) return fail(MIMO_EUNSUPPORTED, "unknown dtype %d", dt);
+  if (B < 1 || Hq < 1 || Hkv < 1) return fail(MIMO_EINVAL, "B, Hq and Hkv must be >= 1");
+  if (Hq % Hkv) return fail(MIMO_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (Hq > mimo::kMaxHeads) return fail(MIMO_EUNSUPPORTED, "Hq %d exceeds %d", Hq, mimo::kMaxHeads);
+  if (window < 1) return fail(MIMO_EINVAL, "window must be >= 1 (got %d)", window);
+  if (!std::isfinite(scale)) return fail(MIMO_EINVAL, "scale must be finite");
+  if (d_qk != 192 || d_v != 128)
+    return fail(MIMO_EUNSUPPORTED, "head dims (%d, %d) unsupported; this build has (192, 128)", d_qk, d_v);
+  return MIMO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mimo_attn_last_error(void) { return g_err.c_str(); }
+
+int mimo_attn_version(void) { return 10000; }
+
+int mimo_attn_prefill(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v,
+                      const void* q, const void* k, const void* v, int window, const float* sink,
+                      const int32_t* kv_head_of_q, float scale, void* o, float* lse,
+                      hipStream_t stream) {
+  g_err.clear();
+  if (int rc = check_common(dt, B, Hq, Hkv, d_qk, d_v, window, scale)) return rc;
+  if (L < 1) return fail(MIMO_EINVAL, "L must be >= 1");
+  if (L > (1 << 30)) return fail(MIMO_EUNSUPPORTED, "L %d exceeds 2^30", L);
+  if (!q || !k || !v || !o) return fail(MIMO_EINVAL, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(MIMO_EINVAL, "q, k, v and o must be 16-byte aligned");
+  if ((sink && !aligned4(sink)) || (lse && !aligned4(lse)))
+    return fail(MIMO_EINVAL, "sink and lse must be 4-byte aligned");
+  const double elem = dt == MIMO_BF16 ? 2.0 : 4.0;
+  if ((double)B * L * Hq * d_qk * elem > 4.6e18) return fail(MIMO_EINVAL, "tensor too large");
+
+  mimo::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.sink = sink;
+  a.B = B; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.window = window < L ? window : L;
+  a.scale_log2 = scale * mimo::kLog2e;
+  if (int rc = group_heads(Hq, Hkv, kv_head_of_q, &a.hl)) return rc;
+  const hipError_t e = mimo::prefill_launch(dt == MIMO_BF16, a, stream);
+  if (e != hipSuccess) return fail(MIMO_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return MIMO_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+struct DecodePlan {
+  int window;          // clamped
+  int nsplit;          // >= 1
+  int keys_per_split;  // multiple of 32
+  size_t ws_bytes;
+};
+
+// Splits: one workgroup per (sequence, KV head) already fills the chip when there are >= 1024
+// pairs; otherwise split the longest key list so that about 2048 workgroups run, keeping each
+// split at >= 256 keys. An explicit request is honoured up to one 32-key block per split.
+DecodePlan plan_decode(int B, int T, int Hq, int Hkv, int max_len, int window, int num_splits) {
+  DecodePlan p{};
+  const long long wmax = (long long)max_len + T;
+  p.window = window < wmax ? window : (int)wmax;
+  const long long list_max = (long long)(max_len < p.window - 1 ? max_len : p.window - 1) + T;
+  const long long blocks = (list_max + 31) / 32;
+  long long ns;
+  if (num_splits > 0) {
+    ns = num_splits;
+  } else {
+    const long long pairs = (long long)B * Hkv;
+    ns = pairs >= 1024 ? 1 : (2048 + pairs - 1) / pairs;
+    const long long cap = (list_max + 255) / 256;
+    if (ns > cap) ns = cap;
+  }
+  if (ns > blocks) ns = blocks;
+  if (ns < 1) ns = 1;
+  const long long kps_blocks = (blocks + ns - 1) / ns;
+  p.keys_per_split = (int)(kps_blocks * 32);
+  p.nsplit = (int)((list_max + p.keys_per_split - 1) / p.keys_per_split);
+  const int G = Hq / Hkv;
+  p.ws_bytes = mimo::decode_ws_bytes(B, Hkv, G * T, p.nsplit);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mimo_attn_decode_workspace_size(int B, int T, int Hq, int Hkv, int d_v, int max_cache_len,
+                                       int window, int num_splits) {
+  if (B < 1 || T < 1 || T > 4 || Hq < 1 || Hkv < 1 || Hq % Hkv || d_v != 128 || max_cache_len < 0 ||
+      window < 1 || num_splits < 0 || (Hq / Hkv) * T > mimo::kMaxCols)
+    return 0;
+  return plan_decode(B, T, Hq, Hkv, max_cache_len, window, num_splits).ws_bytes;
+}
+
+int mimo_attn_decode(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
+                     const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                     const void* v_cache, int C, const int32_t* cache_len,
+                     const int32_t* cache_offset, int max_cache_len, int window,
+                     const float* sink, const int32_t* kv_head_of_q, float scale, int num_splits,
+                     void* workspace, size_t workspace_bytes, void* o, float* lse,
+                     hipStream_t stream) {
+  g_err.clear();
+  if (int rc = check_common(dt, B, Hq, Hkv, d_qk, d_v, window, scale)) return rc;
+  if (T < 1 || T > 4) return fail(MIMO_EINVAL, "T must be in 1..4 (got %d)", T);
+  if ((Hq / Hkv) * T > mimo::kMaxCols)
+    return fail(MIMO_EUNSUPPORTED, "(Hq/Hkv) * T = %d exceeds %d query columns per KV head",
+                (Hq / Hkv) * T, mimo::kMaxCols);
+  if (max_cache_len < 0 || max_cache_len > (1 << 30) - 8)
+    return fail(MIMO_EINVAL, "max_cache_len %d outside [0, 2^30 - 8]", max_cache_len);
+  if (C < 1) return fail(MIMO_EINVAL, "C must be >= 1");
+  const int need = (window - 1 < max_cache_len) ? window - 1 : max_cache_len;
+  if (C < need)
+    return fail(MIMO_EINVAL, "cache of %d slots cannot hold the %d committed keys a window of %d needs",
+                C, need, window);
+  if (num_splits < 0) return fail(MIMO_EINVAL, "num_splits must be >= 0");
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !o || !cache_len)
+    return fail(MIMO_EINVAL, "q, k_new, v_new, k_cache, v_cache, cache_len and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(o))
+    return fail(MIMO_EINVAL, "q, k_new, v_new, k_cache, v_cache and o must be 16-byte aligned");
+  if (!aligned4(cache_len) || (cache_offset && !aligned4(cache_offset)) || (sink && !aligned4(sink)) ||
+      (lse && !aligned4(lse)))
+    return fail(MIMO_EINVAL, "cache_len, cache_offset, sink and lse must be 4-byte aligned");
+  const double elem = dt == MIMO_BF16 ? 2.0 : 4.0;
+  if ((double)B * C * Hkv * d_qk * elem > 4.6e18) return fail(MIMO_EINVAL, "cache too large");
+
+  const DecodePlan plan = plan_decode(B, T, Hq, Hkv, max_cache_len, window, num_splits);
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes)
+      return fail(MIMO_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                  plan.ws_bytes);
+    if (!aligned16(workspace)) return fail(MIMO_EINVAL, "workspace must be 16-byte aligned");
+  }
+
+  mimo::DecodeArgs a{};
+  a.q = q; a.k_new = k_new; a.v_new = v_new; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.cache_len = cache_len; a.cache_offset = cache_offset; a.sink = sink;
+  a.o = o; a.lse = lse; a.ws = static_cast<float*>(workspace);
+  a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.C = C;
+  a.max_len = max_cache_len;
+  a.window = plan.window;
+  a.scale_log2 = scale * mimo::kLog2e;
+  a.nsplit = plan.nsplit;
+  a.keys_per_split = plan.keys_per_split;
+  a.ncols = a.G * T;
+  if (int rc = group_heads(Hq, Hkv, kv_head_of_q, &a.hl)) return rc;
+  const hipError_t e = mimo::decode_launch(dt == MIMO_BF16, a, stream);
+  if (e != hipSuccess) return fail(MIMO_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+  return MIMO_OK;
+}
+
+}  // extern "C"

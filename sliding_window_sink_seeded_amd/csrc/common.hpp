@@ -1,0 +1,124 @@
+// Device helpers shared by the prefill and decode kernels (gfx950 / CDNA4, wave64).
+//
+// MFMA data layout used throughout (32x32 tiles):
+//   * A operand (32 x 16): lane l supplies row (l % 32) and 8 contraction elements.
+//   * B operand (16 x 32): lane l supplies column (l % 32) and 8 contraction elements.
+//   * C/D (32 x 32, 16 fp32 per lane): lane l holds column (l % 32); register r holds row
+//     8 * (r / 4) + 4 * (l / 32) + (r % 4).
+// Which contraction index each of a lane's 8 elements stands for does not matter as long as the A
+// and B operands of one product use the same assignment, because the product sums over it. The
+// kernels therefore pick the assignment that makes their loads contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mimo {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxHeads = 256;
+
+// Storage tag types. Memory holds raw bits; fragments are what the MFMA consumes.
+struct BF16 {
+  using Frag = bf16x8;  // 8 contraction elements per lane, 16 bytes
+  static constexpr int kBytes = 2;
+  static constexpr int kPerChunk = 8;  // elements per 16-byte chunk
+};
+struct F32 {
+  using Frag = f32x8;  // 8 contraction elements per lane, 32 bytes
+  static constexpr int kBytes = 4;
+  static constexpr int kPerChunk = 4;
+};
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// acc += A(32x16) * B(16x32) with 8 contraction elements per lane.
+__device__ __forceinline__ f32x16 mma(const bf16x8& a, const bf16x8& b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+// fp32: eight 32x32x2 products; product e contracts element e of both lane halves.
+__device__ __forceinline__ f32x16 mma(const f32x8& a, const f32x8& b, f32x16 acc) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], acc, 0, 0, 0);
+  return acc;
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs; NaN is not produced by the kernels).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+
+template <typename E>
+__device__ __forceinline__ typename E::Frag frag_from_f32(const float* x);
+template <>
+__device__ __forceinline__ bf16x8 frag_from_f32<BF16>(const float* x) {
+  u32x4 u;
+  u[0] = pack_bf16x2(x[0], x[1]);
+  u[1] = pack_bf16x2(x[2], x[3]);
+  u[2] = pack_bf16x2(x[4], x[5]);
+  u[3] = pack_bf16x2(x[6], x[7]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+template <>
+__device__ __forceinline__ f32x8 frag_from_f32<F32>(const float* x) {
+  f32x8 f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = x[i];
+  return f;
+}
+
+// Fragment from 8 consecutive accumulator registers starting at `off` (compile-time after unroll).
+template <typename E>
+__device__ __forceinline__ typename E::Frag frag_from_acc(const f32x16& s, int off) {
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = s[off + i];
+  return frag_from_f32<E>(x);
+}
+
+// Reductions across the two halves of a wave: lane l and lane l ^ 32 both receive
+// op(x[l % 32], x[l % 32 + 32]). permlane32_swap hands each lane the values of both halves at its
+// position, so a symmetric op of its two results is the cross-half reduction in either half.
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x4 zero_chunk() {
+  u32x4 z;
+  z[0] = z[1] = z[2] = z[3] = 0u;
+  return z;
+}
+
+// Query heads grouped by KV head: heads[g * G + j] is the j-th query head served by KV head g.
+struct HeadList {
+  int16_t heads[kMaxHeads];
+};
+
+}  // namespace mimo

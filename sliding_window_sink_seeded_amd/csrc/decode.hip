@@ -1,0 +1,394 @@
+// Decode / MTP-verify kernels: a few new tokens per sequence against a ring (sliding-window) or
+// linear (global) KV cache, split-KV with a sink-once combine.
+//
+// Operation: MiMo-V2-Flash Technical Report review (xllm-io), §3.1-§3.2 (window, GQA, head dims,
+// per-head sink); MiMo series notes (plmsmile), MiMo-V2-Flash > local window (the sliding-window
+// cache does not grow with history) and > lightweight MTP > inference (the main model verifies the
+// drafted tokens in parallel, so one step carries 1 + drafts queries per sequence).
+//
+// Keys of sequence b form one logical list: committed positions [max(0, P - W + 1), P) read from
+// slot (p + off) mod C, then the T new tokens at positions P .. P+T-1. New token t sees positions
+// in [P + t - W + 1, P + t].
+//
+// Work decomposition: one workgroup per (split, KV head g, sequence b). The G*T query columns of
+// (b, g) - every query head of the group times every new token - are the MFMA columns (32 per
+// column block), so each K/V element read from HBM serves all of them. The split's keys are cut
+// into 32-key blocks dealt round-robin to the waves. A wave keeps an online softmax per column
+// (no sink here), then the waves of the workgroup merge through LDS in a fixed order:
+//   * single pass (one split): the sink joins the merge and O / LSE are written;
+//   * several splits: the merged, unnormalised (m, l, acc) go to the workspace and
+//     combine_kernel folds the splits and the sink (counted once) into O / LSE.
+#include "launch.hpp"
+
+namespace mimo {
+
+constexpr int kDDQK = 192;
+constexpr int kDDV = 128;
+constexpr int kDecNW = 4;      // waves per workgroup
+
+template <typename E, int NCB>
+struct DecodeLds {
+  static constexpr int kQStride = kDDQK + 16 / E::kBytes;  // Q^T rows (one per column), padded
+  static constexpr int kQBytes = NCB * 32 * kQStride * E::kBytes;
+  static constexpr int kVStride = 32 + 4;  // V^T rows of one 32-key block
+  static constexpr int kVBytes = kDDV * kVStride * E::kBytes;
+  static constexpr int kMergeBytes = kDecNW * (kDDV / 32) * 16 * 64 * 4;  // one column block
+  static constexpr int kWorkBytes = kDecNW * kVBytes > kMergeBytes ? kDecNW * kVBytes : kMergeBytes;
+  static constexpr int kBytes = kQBytes + kWorkBytes + kDecNW * 64 * 4 * 2;
+};
+
+// Address of key row `pos` (logical position) of sequence b / KV head g.
+__device__ __forceinline__ const char* key_row(const char* cache, const char* fresh, size_t row_bytes,
+                                               int Hkv, int C, int T, int b, int g, int P, int off,
+                                               int pos) {
+  if (pos < P) {
+    long long slot = ((long long)pos + off) % C;
+    if (slot < 0) slot += C;
+    return cache + (((size_t)b * C + (size_t)slot) * Hkv + g) * row_bytes;
+  }
+  return fresh + (((size_t)b * T + (size_t)(pos - P)) * Hkv + g) * row_bytes;
+}
+
+template <typename E, int NCB>
+__global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a) {
+  using Frag = typename E::Frag;
+  using Lds = DecodeLds<E, NCB>;
+  __shared__ __attribute__((aligned(16))) char smem[Lds::kBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int wave = tid >> 6;
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+
+  int P = a.cache_len[b];
+  P = P < 0 ? 0 : (P > a.max_len ? a.max_len : P);
+  const int off = a.cache_offset ? a.cache_offset[b] : 0;
+  const int list0 = max(0, P - a.window + 1);
+  const int list1 = P + a.T;
+  const int s0 = list0 + split * a.keys_per_split;
+  const int s1 = min(list1, s0 + a.keys_per_split);
+
+  const size_t krow_bytes = (size_t)kDDQK * E::kBytes;
+  const size_t vrow_bytes = (size_t)kDDV * E::kBytes;
+
+  // Q^T of every query column (head j of the group x new token t, column c = j * T + t) -> LDS.
+  char* sq = smem;
+  {
+    constexpr int kChunksRow = kDDQK / E::kPerChunk;
+    for (int u = tid; u < NCB * 32 * kChunksRow; u += kDecNW * 64) {
+      const int c = u / kChunksRow, ch = u % kChunksRow;
+      u32x4 x = zero_chunk();
+      if (c < a.ncols) {
+        const int head = a.hl.heads[g * a.G + c / a.T];
+        x = ld16((const char*)a.q + (((size_t)b * a.T + c % a.T) * a.Hq + head) * krow_bytes + ch * 16);
+      }
+      st16(sq + c * Lds::kQStride * E::kBytes + ch * 16, x);
+    }
+  }
+  int qpos[NCB];
+  float m[NCB], l[NCB];
+  f32x16 acc[NCB][kDDV / 32];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int c = cb * 32 + col;
+    qpos[cb] = c < a.ncols ? P + c % a.T : -(1 << 30);  // padding columns see no key
+    m[cb] = -INFINITY;
+    l[cb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < kDDV / 32; ++db) acc[cb][db] = zero16();
+  }
+  __syncthreads();
+
+  char* work = smem + Lds::kQBytes;
+  char* my_vt = work + wave * Lds::kVBytes;
+  for (int key0 = s0 + 32 * wave; key0 < s1; key0 += 32 * kDecNW) {
+    // V block -> LDS, transposed to [dv][key]; unit = 4 keys x one 16-byte dv chunk.
+    constexpr int kVChunksRow = kDDV / E::kPerChunk;
+    constexpr int kUnits = 8 * kVChunksRow;
+#pragma unroll
+    for (int i = 0; i < kUnits / 64; ++i) {
+      const int u = lane + 64 * i;
+      const int kg = u / kVChunksRow, dc = u % kVChunksRow;
+      u32x4 vr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pos = key0 + 4 * kg + r;
+        vr[r] = zero_chunk();
+        if (pos < s1)
+          vr[r] = ld16(key_row((const char*)a.v_cache, (const char*)a.v_new, vrow_bytes, a.Hkv, a.C,
+                               a.T, b, g, P, off, pos) + dc * 16);
+      }
+      if constexpr (E::kBytes == 2) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          uint32_t e[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) e[r] = (d & 1) ? (vr[r][d / 2] >> 16) : (vr[r][d / 2] & 0xFFFFu);
+          u32x2 w;
+          w[0] = e[0] | (e[1] << 16);
+          w[1] = e[2] | (e[3] << 16);
+          *reinterpret_cast<u32x2*>(my_vt + ((dc * 8 + d) * Lds::kVStride + 4 * kg) * 2) = w;
+        }
+      } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          u32x4 w;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[r] = vr[r][d];
+          st16(my_vt + ((dc * 4 + d) * Lds::kVStride + 4 * kg) * 4, w);
+        }
+      }
+    }
+
+    // S^T = K Q^T: K rows come straight from memory as A fragments (key = key0 + col).
+    f32x16 s[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) s[cb] = zero16();
+    {
+      const int pos = key0 + col;
+      const bool kvalid = pos < s1;
+      const char* krow = kvalid ? key_row((const char*)a.k_cache, (const char*)a.k_new, krow_bytes,
+                                          a.Hkv, a.C, a.T, b, g, P, off, pos)
+                                : (const char*)a.k_new;
+#pragma unroll
+      for (int kk = 0; kk < kDDQK / 16; ++kk) {
+        const char* p = krow + (16 * kk + 8 * half) * E::kBytes;
+        Frag kf;
+        if constexpr (E::kBytes == 2) {
+          kf = __builtin_bit_cast(bf16x8, kvalid ? ld16(p) : zero_chunk());
+        } else {
+          const u32x4 x = kvalid ? ld16(p) : zero_chunk();
+          const u32x4 y = kvalid ? ld16(p + 16) : zero_chunk();
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            kf[i] = __uint_as_float(x[i]);
+            kf[4 + i] = __uint_as_float(y[i]);
+          }
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const char* qp = sq + ((cb * 32 + col) * Lds::kQStride + 16 * kk + 8 * half) * E::kBytes;
+          Frag qf;
+          if constexpr (E::kBytes == 2) {
+            qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp));
+          } else {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(qp);
+            const f32x4 y = *reinterpret_cast<const f32x4*>(qp + 16);
+            qf[0] = x[0]; qf[1] = x[1]; qf[2] = x[2]; qf[3] = x[3];
+            qf[4] = y[0]; qf[5] = y[1]; qf[6] = y[2]; qf[7] = y[3];
+          }
+          s[cb] = mma(kf, qf, s[cb]);
+        }
+      }
+    }
+
+    // The V^T block was written by other lanes of this wave: order those writes before the reads.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int pos = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int d = qpos[cb] - pos;
+        const float t = (d >= 0 && d < a.window && pos < s1) ? s[cb][r] * a.scale_log2 : -INFINITY;
+        s[cb][r] = t;
+        bmax = fmaxf(bmax, t);
+      }
+      bmax = halves_max(bmax);
+      const float m_new = fmaxf(m[cb], bmax);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m[cb] - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(s[cb][r] - m_use);
+        s[cb][r] = p;
+        rs += p;
+      }
+      rs = halves_sum(rs);
+      l[cb] = l[cb] * alpha + rs;
+      m[cb] = m_new;
+#pragma unroll
+      for (int db = 0; db < kDDV / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[cb][db][r] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const Frag pf = frag_from_acc<E>(s[cb], 8 * ks);
+#pragma unroll
+        for (int db = 0; db < kDDV / 32; ++db) {
+          const char* p = my_vt + ((32 * db + col) * Lds::kVStride + 16 * ks + 4 * half) * E::kBytes;
+          Frag vf;
+          if constexpr (E::kBytes == 2) {
+            const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+            const u32x2 y = *reinterpret_cast<const u32x2*>(p + 16);
+            u32x4 u;
+            u[0] = x[0]; u[1] = x[1]; u[2] = y[0]; u[3] = y[1];
+            vf = __builtin_bit_cast(bf16x8, u);
+          } else {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+            const f32x4 y = *reinterpret_cast<const f32x4*>(p + 32);
+            vf[0] = x[0]; vf[1] = x[1]; vf[2] = x[2]; vf[3] = x[3];
+            vf[4] = y[0]; vf[5] = y[1]; vf[6] = y[2]; vf[7] = y[3];
+          }
+          acc[cb][db] = mma(vf, pf, acc[cb][db]);
+        }
+      }
+    }
+    // The next block rewrites this wave's V^T buffer: finish every read of it first.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- merge the waves of this workgroup, one column block at a time (fixed order) ----
+  float* sm_acc = reinterpret_cast<float*>(work);  // [wave][db][r][lane]
+  float* sm_m = reinterpret_cast<float*>(smem + (Lds::kBytes - kDecNW * 64 * 4 * 2));
+  float* sm_l = sm_m + kDecNW * 64;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    __syncthreads();  // previous users of the work area are done
+    sm_m[wave * 64 + lane] = m[cb];
+    __syncthreads();
+    const int c = cb * 32 + col;
+    const bool cvalid = c < a.ncols;
+    const int t = cvalid ? c % a.T : 0;
+    const int head = cvalid ? a.hl.heads[g * a.G + c / a.T] : 0;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecNW; ++w) M = fmaxf(M, sm_m[w * 64 + lane]);
+    const bool fold_sink = (a.nsplit == 1) && a.sink && cvalid;
+    const float s_l2 = fold_sink ? a.sink[head] * kLog2e : -INFINITY;
+    M = fmaxf(M, s_l2);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    const float scale_w = fast_exp2(m[cb] - M_use);
+#pragma unroll
+    for (int db = 0; db < kDDV / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm_acc[((wave * (kDDV / 32) + db) * 16 + r) * 64 + lane] = acc[cb][db][r] * scale_w;
+    sm_l[wave * 64 + lane] = l[cb] * scale_w;
+    __syncthreads();
+    float L = fold_sink ? fast_exp2(s_l2 - M_use) : 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecNW; ++w) L += sm_l[w * 64 + lane];
+    // wave w reduces dv block db = w (kDecNW == kDDV / 32)
+    const int db = wave;
+    f32x16 o = zero16();
+#pragma unroll
+    for (int w = 0; w < kDecNW; ++w)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[r] += sm_acc[((w * (kDDV / 32) + db) * 16 + r) * 64 + lane];
+    if (cvalid && a.nsplit == 1) {
+      const float inv = 1.f / L;
+      char* orow = (char*)a.o + (((size_t)b * a.T + t) * a.Hq + head) * kDDV * E::kBytes;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int dv = 32 * db + 8 * gq + 4 * half;
+        const float x0 = o[4 * gq] * inv, x1 = o[4 * gq + 1] * inv;
+        const float x2 = o[4 * gq + 2] * inv, x3 = o[4 * gq + 3] * inv;
+        if constexpr (E::kBytes == 2) {
+          u32x2 w;
+          w[0] = pack_bf16x2(x0, x1);
+          w[1] = pack_bf16x2(x2, x3);
+          *reinterpret_cast<u32x2*>(orow + dv * 2) = w;
+        } else {
+          f32x4 w;
+          w[0] = x0; w[1] = x1; w[2] = x2; w[3] = x3;
+          *reinterpret_cast<f32x4*>(orow + dv * 4) = w;
+        }
+      }
+      if (a.lse && wave == 0 && half == 0)
+        a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(L)) * kLn2;
+    } else if (cvalid) {
+      // partial record for (b, g, split, column c): acc[kDDV], m, l
+      const int ncols_pad = NCB * 32;
+      float* rec = a.ws + ((((size_t)b * a.Hkv + g) * a.nsplit + split) * ncols_pad + c) * (kDDV + 2);
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int dv = 32 * db + 8 * gq + 4 * half;
+        f32x4 w;
+        w[0] = o[4 * gq]; w[1] = o[4 * gq + 1]; w[2] = o[4 * gq + 2]; w[3] = o[4 * gq + 3];
+        float* dst = rec + dv;  // records are only 8-byte aligned (kDDV + 2 floats each)
+        dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2]; dst[3] = w[3];
+      }
+      if (wave == 0 && half == 0) {
+        rec[kDDV] = M;
+        rec[kDDV + 1] = L;
+      }
+    }
+  }
+}
+
+// One workgroup of kDDV threads per output row (b, t, head): fold the split partials and the
+// sink (once) into O and LSE.
+template <typename E>
+__global__ __launch_bounds__(kDDV) void combine_kernel(const DecodeArgs a) {
+  const int c = blockIdx.x;  // query column within the group
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int dv = threadIdx.x;
+  const int ncols_pad = ((a.ncols + 31) / 32) * 32;
+  const int t = c % a.T;
+  const int head = a.hl.heads[g * a.G + c / a.T];
+  const float* base = a.ws + (((size_t)b * a.Hkv + g) * a.nsplit * ncols_pad + c) * (kDDV + 2);
+  const size_t stride = (size_t)ncols_pad * (kDDV + 2);
+
+  float M = a.sink ? a.sink[head] * kLog2e : -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, base[s * stride + kDDV]);
+  const float M_use = (M == -INFINITY) ? 0.f : M;
+  float L = a.sink ? fast_exp2(a.sink[head] * kLog2e - M_use) : 0.f;
+  float o = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float* rec = base + s * stride;
+    const float w = fast_exp2(rec[kDDV] - M_use);  // empty split: m = -inf -> weight 0
+    L += rec[kDDV + 1] * w;
+    o += rec[dv] * w;
+  }
+  o /= L;
+  char* orow = (char*)a.o + (((size_t)b * a.T + t) * a.Hq + head) * kDDV * E::kBytes;
+  if constexpr (E::kBytes == 2) {
+    reinterpret_cast<uint16_t*>(orow)[dv] = (uint16_t)bf16_bits(o);
+  } else {
+    reinterpret_cast<float*>(orow)[dv] = o;
+  }
+  if (a.lse && dv == 0) a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(L)) * kLn2;
+}
+
+size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit) {
+  if (nsplit <= 1) return 0;
+  const size_t ncols_pad = (size_t)((ncols + 31) / 32) * 32;
+  return (size_t)B * Hkv * nsplit * ncols_pad * (kDDV + 2) * sizeof(float);
+}
+
+hipError_t decode_launch(bool bf16, const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.nsplit, a.Hkv, a.B);
+  const dim3 block(kDecNW * 64);
+  const bool two = a.ncols > 32;
+  if (bf16 && two)
+    hipLaunchKernelGGL((decode_kernel<BF16, 2>), grid, block, 0, stream, a);
+  else if (bf16)
+    hipLaunchKernelGGL((decode_kernel<BF16, 1>), grid, block, 0, stream, a);
+  else if (two)
+    hipLaunchKernelGGL((decode_kernel<F32, 2>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<F32, 1>), grid, block, 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  const dim3 cgrid(a.ncols, a.Hkv, a.B);
+  if (bf16)
+    hipLaunchKernelGGL(combine_kernel<BF16>, cgrid, dim3(kDDV), 0, stream, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<F32>, cgrid, dim3(kDDV), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mimo

@@ -1,0 +1,57 @@
+// Argument blocks and launchers shared by the host API and the kernels.
+#pragma once
+
+#include "common.hpp"
+
+namespace mimo {
+
+constexpr int kMaxCols = 64;  // decode: query columns (query heads per KV head x new tokens)
+
+// Prefill arguments (kernel argument block, passed by value).
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const float* sink;
+  int B, L, Hq, Hkv, G;
+  int window;        // clamped to <= L by the host
+  float scale_log2;  // scale * log2(e)
+  int heads_per_wg;  // HG
+  int n_qblocks;     // ceil(L / (32 * NW / HG))
+  int n_hchunks;     // G / HG
+  HeadList hl;
+};
+
+// Decode arguments (kernel argument block, passed by value).
+struct DecodeArgs {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cache_len;
+  const int32_t* cache_offset;
+  const float* sink;
+  void* o;
+  float* lse;
+  float* ws;  // [B][Hkv][nsplit][ncols_pad][kDDV + 2] fp32 when nsplit > 1
+  int B, T, Hq, Hkv, G, C;
+  int max_len;
+  int window;  // clamped to <= max_len + T by the host
+  float scale_log2;
+  int nsplit;
+  int keys_per_split;  // multiple of 32
+  int ncols;           // G * T
+  HeadList hl;
+};
+
+// Picks the prefill variant (fills the tiling fields of `a`) and launches it on `stream`.
+hipError_t prefill_launch(bool bf16, PrefillArgs a, hipStream_t stream);
+// Launches the decode kernel and, when a.nsplit > 1, the combine kernel on `stream`.
+hipError_t decode_launch(bool bf16, const DecodeArgs& a, hipStream_t stream);
+// Workspace bytes for nsplit > 1 partial records (0 otherwise).
+size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit);
+
+}  // namespace mimo
