@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark of the sink-seeded SWA / global attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the attention over one batch of seeded synthetic input already resident in
+HBM. The headline workload is the sliding-window bf16 prefill (batch 4 x 32768, 64/8 heads, W=128):
+`value` is algorithmic TFLOP/s (only visible scores, 640 FLOP each) over the wall clock of the K
+timed steps. One JSON line goes to stdout, with:
+
+* roofline - the dominant kernel's algorithmic bytes (or FLOPs) per launch divided by its average
+  launch duration, timed with HIP events on the launch stream, against MI355X's published peak;
+* cpu_baseline - the float64 oracle timed on the host on a bounded leading slice of the same
+  workload (a reported baseline, not a target);
+* secondary - the other measured workloads (global prefill, ring decode, split-KV global decode),
+  timed the same way, with decode inputs rotated over enough copies to defeat the 256 MiB MALL.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA peaks, TFLOP/s
+MALL_BYTES = 256 << 20
+
+METRIC = "prefill attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Case:
+    """Seeded inputs for one workload, uploaded once (plus rotated copies), and its launcher."""
+
+    def __init__(self, w, rotate_to_defeat_mall=True):
+        import numpy as np
+        import torch
+
+        import sliding_window_sink_seeded_amd as mimo
+        from sliding_window_sink_seeded_amd import inputs, workloads
+
+        self.w = w
+        self.mimo = mimo
+        dt = w.dtype
+        t0 = time.perf_counter()
+        if w.kind == "prefill":
+            self.inp = inputs.prefill_inputs(w.seed, w.B, w.L, w.Hq, w.Hkv, w.dqk, w.dv, w.window, dt)
+            self.lens = None
+            self.flops, self.bytes = workloads.algorithmic(w)
+        else:
+            self.inp = inputs.decode_inputs(w.seed, w.B, w.T, w.Hq, w.Hkv, w.dqk, w.dv, w.C, w.window,
+                                            dt, cache_len=(w.P or None),
+                                            len_range=(w.len_range or None),
+                                            ring_offsets=w.ring_offsets)
+            self.lens = self.inp.cache_len
+            self.flops, self.bytes = workloads.algorithmic(w, self.lens)
+        log(f"[bench] {w.name}: inputs generated in {time.perf_counter() - t0:.1f} s")
+        up = lambda x: inputs.to_torch(x, dt)
+        n_sets = 1
+        if rotate_to_defeat_mall and self.bytes < 4 * MALL_BYTES:
+            n_sets = min(16, max(2, math.ceil(8 * MALL_BYTES / self.bytes)))
+        self.sink = torch.from_numpy(self.inp.sink).cuda()
+        self.sets = []
+        if w.kind == "prefill":
+            base = [up(self.inp.q), up(self.inp.k), up(self.inp.v)]
+            for i in range(n_sets):
+                ts = base if i == 0 else [t.clone() for t in base]
+                o = torch.empty(w.B, w.L, w.Hq, w.dv, dtype=ts[0].dtype, device="cuda")
+                self.sets.append((ts, o))
+        else:
+            base = [up(self.inp.q), up(self.inp.k_new), up(self.inp.v_new), up(self.inp.k_cache),
+                    up(self.inp.v_cache)]
+            self.len_t = torch.from_numpy(self.inp.cache_len).cuda()
+            self.off_t = (torch.from_numpy(self.inp.cache_offset).cuda()
+                          if self.inp.cache_offset is not None else None)
+            self.max_len = int(w.P or w.len_range[1])
+            nb = mimo.decode_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.dv, self.max_len, w.window)
+            self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+            for i in range(n_sets):
+                ts = base if i == 0 else [t.clone() for t in base]
+                o = torch.empty(w.B, w.T, w.Hq, w.dv, dtype=ts[0].dtype, device="cuda")
+                self.sets.append((ts, o))
+        self.n_sets = n_sets
+        self.i = 0
+        torch.cuda.synchronize()
+
+    def run(self):
+        ts, o = self.sets[self.i % self.n_sets]
+        self.i += 1
+        w = self.w
+        if w.kind == "prefill":
+            self.mimo.prefill(ts[0], ts[1], ts[2], w.window, sink=self.sink, scale=self.inp.scale, out=o)
+        else:
+            self.mimo.decode(ts[0], ts[1], ts[2], ts[3], ts[4], self.len_t, w.window, self.max_len,
+                             cache_offset=self.off_t, sink=self.sink, scale=self.inp.scale,
+                             workspace=self.ws, out=o)
+        return o
+
+    def time(self, steps, warmup):
+        import torch
+
+        for _ in range(warmup):
+            self.run()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        for _ in range(steps):
+            self.run()
+        ev1.record()
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        event_ms = ev0.elapsed_time(ev1) / steps
+        return wall_ms, event_ms
+
+    def sampled_parity(self, n_rows=8):
+        """Compare a few output rows (all heads) with the oracle; returns error metrics."""
+        import numpy as np
+        import torch
+
+        import oracle
+        from sliding_window_sink_seeded_amd.inputs import as_float
+
+        w, inp, dt = self.w, self.inp, self.w.dtype
+        self.i = 0  # every rotated set holds the same inputs; use the first
+        o = self.run()
+        torch.cuda.synchronize()
+        if w.kind == "prefill":
+            rng = np.random.default_rng(0)
+            pos = sorted({0, w.L - 1, min(w.L - 1, 127), min(w.L - 1, 128),
+                          *rng.integers(0, w.L, n_rows - 4).tolist()})
+            rows = [(int(b), int(i)) for b, i in zip(rng.integers(0, w.B, len(pos)), pos)]
+            got = np.stack([o[b, i].float().cpu().numpy() for b, i in rows])
+            ref = []
+            for b, i in rows:
+                # row i sees keys [lo, i]: it is the last row of that slice of the sequence
+                lo = max(0, i - w.window + 1)
+                rq = _pad_q(as_float(inp.q[b:b + 1, i:i + 1], dt), i - lo)
+                rk = as_float(inp.k[b:b + 1, lo:i + 1], dt)
+                rv = as_float(inp.v[b:b + 1, lo:i + 1], dt)
+                ro, _ = oracle.prefill_rows(rq, rk, rv, w.window, inp.sink, inp.scale, [(0, i - lo)])
+                ref.append(ro[0])
+            ref = np.stack(ref)
+        else:
+            seqs = [0, w.B - 1]
+            keep = list(range(0, w.Hq, 7))
+            got = o[seqs].float().cpu().numpy()[:, :, keep]
+            ref, _ = oracle.decode(as_float(inp.q[seqs], dt), as_float(inp.k_new[seqs], dt),
+                                   as_float(inp.v_new[seqs], dt), as_float(inp.k_cache[seqs], dt),
+                                   as_float(inp.v_cache[seqs], dt), inp.cache_len[seqs],
+                                   None if inp.cache_offset is None else inp.cache_offset[seqs],
+                                   w.window, inp.sink, inp.scale, heads=keep)
+            ref = ref[:, :, keep]
+        d = got.astype(np.float64) - ref
+        return {"rows": int(np.prod(got.shape[:-1])), "abs_max": float(np.abs(d).max()),
+                "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref))}
+
+
+def _pad_q(rq, n_before):
+    """Place one query row at slice position n_before (earlier rows are never read)."""
+    import numpy as np
+
+    q = np.zeros((1, n_before + 1) + rq.shape[2:], dtype=rq.dtype)
+    q[:, n_before] = rq[:, 0]
+    return q
+
+
+def cpu_baseline(case, target_s=12.0):
+    """Float64 oracle on the host over a leading slice of sequence 0 (exact for those rows)."""
+    import numpy as np
+
+    import oracle
+    from sliding_window_sink_seeded_amd import workloads
+    from sliding_window_sink_seeded_amd.inputs import as_float
+
+    w, inp, dt = case.w, case.inp, case.w.dtype
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    if w.kind == "prefill":
+        def run(S):
+            q, k, v = (as_float(x[0:1, :S], dt) for x in (inp.q, inp.k, inp.v))
+            t0 = time.perf_counter()
+            oracle.prefill(q, k, v, w.window, inp.sink, inp.scale)
+            return time.perf_counter() - t0, workloads.prefill_scores(1, S, w.Hq, min(w.window, S))
+
+        S = min(w.L, 512)
+        t, _ = run(S)
+        S2 = int(min(w.L, max(S, S * target_s / max(t, 1e-3))))
+        if w.window >= w.L:  # quadratic work in S
+            S2 = int(min(w.L, max(S, S * math.sqrt(target_s / max(t, 1e-3)))))
+        S2 = max(1, (S2 // 256) * 256) if S2 >= 256 else S2
+        t, scores = run(S2)
+        flops = scores * 2 * (w.dqk + w.dv)
+        sample = f"sequence 0, query positions [0, {S2}) of {w.L}, all {w.Hq} heads"
+    else:
+        def run(nseq):
+            sel = list(range(nseq))
+            args = [as_float(x[sel], dt) for x in (inp.q, inp.k_new, inp.v_new, inp.k_cache, inp.v_cache)]
+            t0 = time.perf_counter()
+            oracle.decode(*args, inp.cache_len[sel],
+                          None if inp.cache_offset is None else inp.cache_offset[sel], w.window,
+                          inp.sink, inp.scale)
+            return time.perf_counter() - t0, workloads.decode_scores(inp.cache_len[sel], w.T, w.Hq, w.window)
+
+        n = 1
+        t, _ = run(n)
+        n2 = int(min(w.B, max(1, n * target_s / max(t, 1e-3))))
+        t, scores = run(n2)
+        flops = scores * 2 * (w.dqk + w.dv)
+        sample = f"sequences [0, {n2}) of {w.B}, all {w.Hq} heads and {w.T} tokens"
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample, "seconds": round(t, 2)}
+
+
+def describe(case, wall_ms, event_ms):
+    w = case.w
+    tflops = case.flops / (wall_ms * 1e-3) / 1e12
+    gbs = case.bytes / (event_ms * 1e-3) / 1e9
+    return {
+        "workload": w.name, "ms_per_step": round(wall_ms, 4), "kernel_ms": round(event_ms, 4),
+        "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[w.dtype], 4),
+        "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "algorithmic_flop": case.flops, "algorithmic_bytes": case.bytes,
+        "rotated_input_sets": case.n_sets,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="swa_prefill_bf16")
+    ap.add_argument("--no-secondary", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sliding_window_sink_seeded_amd import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = workloads.WORKLOADS[args.workload]
+
+    case = Case(w)
+    wall_ms, event_ms = case.time(args.steps, args.warmup)
+    head = describe(case, wall_ms, event_ms)
+    log(f"[bench] {w.name}: {head}")
+    parity = None if args.no_parity else case.sampled_parity()
+
+    if w.kind == "prefill" and w.window < w.L:
+        bound, unit = "hbm", "GB/s"
+        achieved, peak, per_launch = case.bytes / (event_ms * 1e-3) / 1e9, HBM_PEAK_GBS, case.bytes
+    elif w.kind == "prefill":
+        bound, unit = "mfma", "TFLOP/s"
+        achieved, peak, per_launch = case.flops / (event_ms * 1e-3) / 1e12, MFMA_PEAK_TFLOPS[w.dtype], case.flops
+    else:
+        bound, unit = "hbm", "GB/s"
+        achieved, peak, per_launch = case.bytes / (event_ms * 1e-3) / 1e9, HBM_PEAK_GBS, case.bytes
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "algorithmic_per_launch": per_launch, "kernel_avg_ms": round(event_ms, 4)}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(case)
+    del case
+    torch.cuda.empty_cache()
+
+    secondary = []
+    if not args.no_secondary:
+        for name in ("swa_prefill_f32", "ga_prefill_bf16", "swa_decode_bf16", "ga_decode_bf16"):
+            if name == w.name:
+                continue
+            c = Case(workloads.WORKLOADS[name])
+            sw, se = c.time(max(5, args.steps // 2), 3)
+            d = describe(c, sw, se)
+            log(f"[bench] {name}: {d}")
+            secondary.append(d)
+            del c
+            torch.cuda.empty_cache()
+
+    tflops = head["algorithmic_flop"] / (wall_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs rounded to bf16; sink N(0,1) fp32)",
+        "config": {"workload": w.description, "name": w.name, "batch": w.B, "seq_len": w.L or None,
+                   "q_heads": w.Hq, "kv_heads": w.Hkv, "d_qk": w.dqk, "d_v": w.dv,
+                   "window": w.window, "parallelism": "single GPU"},
+        "mfma_frac": head["mfma_frac"],
+        "hbm_frac": head["hbm_frac"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
