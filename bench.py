@@ -106,11 +106,18 @@ class Case:
                              workspace=self.ws, out=o)
         return o
 
-    def time(self, steps, warmup):
+    def time(self, steps, warmup, min_warm_s=0.25):
+        """W untimed warm-up steps (continued until min_warm_s has passed, so clocks have
+        settled), then exactly `steps` timed steps."""
         import torch
 
-        for _ in range(warmup):
+        t0 = time.perf_counter()
+        n = 0
+        while n < warmup or time.perf_counter() - t0 < min_warm_s:
             self.run()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()

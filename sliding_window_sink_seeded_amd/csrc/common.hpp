@@ -56,14 +56,17 @@ __device__ __forceinline__ f32x16 mma(const f32x8& a, const f32x8& b, f32x16 acc
   return acc;
 }
 
-// Round-to-nearest-even fp32 -> bf16 bits (finite inputs; NaN is not produced by the kernels).
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 pair -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+  f32x2 v;
+  v[0] = lo;
+  v[1] = hi;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return pack_bf16x2(x, 0.f) & 0xFFFFu; }
 
 template <typename E>
 __device__ __forceinline__ typename E::Frag frag_from_f32(const float* x);
@@ -105,15 +108,60 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// v_permlane32_swap: afterwards lanes 32-63 of `a` hold the old lanes 0-31 of `b` and lanes 0-31
+// of `b` hold the old lanes 32-63 of `a`; lanes 0-31 of `a` and 32-63 of `b` are unchanged.
+__device__ __forceinline__ void swap_halves(uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Waits until every outstanding memory operation of this wave has completed.
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ u32x4 zero_chunk() {
   u32x4 z;
   z[0] = z[1] = z[2] = z[3] = 0u;
   return z;
+}
+
+// Packs this lane's query column of a 32 x 128 O^T accumulator block into bf16 output chunks.
+// acc[db][r] holds O[col][32 db + 8 (r / 4) + 4 half + r % 4]. The two wave halves trade register
+// groups so that every lane owns 8 consecutive outputs: chunk i = 2 db + j covers outputs
+// 32 db + 16 j + 8 half .. +7. Every lane must call it (the exchange reads the partner lane).
+__device__ __forceinline__ void pack_row_bf16(const f32x16 (&acc)[4], float inv, u32x4 (&out)[8]) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int g0 = 8 * j, g1 = 8 * j + 4;  // register offsets of groups 2j and 2j+1
+      uint32_t x0 = pack_bf16x2(acc[db][g0] * inv, acc[db][g0 + 1] * inv);
+      uint32_t x1 = pack_bf16x2(acc[db][g0 + 2] * inv, acc[db][g0 + 3] * inv);
+      uint32_t y0 = pack_bf16x2(acc[db][g1] * inv, acc[db][g1 + 1] * inv);
+      uint32_t y1 = pack_bf16x2(acc[db][g1 + 2] * inv, acc[db][g1 + 3] * inv);
+      swap_halves(x0, y0);
+      swap_halves(x1, y1);
+      out[2 * db + j][0] = x0;
+      out[2 * db + j][1] = x1;
+      out[2 * db + j][2] = y0;
+      out[2 * db + j][3] = y1;
+    }
+  }
+}
+__device__ __forceinline__ void store_packed_row_bf16(char* orow, const u32x4 (&out)[8], int half) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(orow + (16 * i + 8 * half) * 2) = out[i];
+}
+// pack + store; lanes with !store write nothing but still take part in the exchange
+__device__ __forceinline__ void store_row_bf16(char* orow, const f32x16 (&acc)[4], float inv,
+                                               int half, bool store) {
+  u32x4 out[8];
+  pack_row_bf16(acc, inv, out);
+  if (store) store_packed_row_bf16(orow, out, half);
 }
 
 // Query heads grouped by KV head: heads[g * G + j] is the j-th query head served by KV head g.

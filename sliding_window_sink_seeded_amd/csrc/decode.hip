@@ -12,19 +12,24 @@
 //
 // Work decomposition: one workgroup per (split, KV head g, sequence b). The G*T query columns of
 // (b, g) - every query head of the group times every new token - are the MFMA columns (32 per
-// column block), so each K/V element read from HBM serves all of them. The split's keys are cut
-// into 32-key blocks dealt round-robin to the waves. A wave keeps an online softmax per column
-// (no sink here), then the waves of the workgroup merge through LDS in a fixed order:
+// column block), so each K/V element read from HBM serves all of them; Q^T sits in LDS, shared
+// by the waves. The split's keys are cut into 32-key blocks dealt round-robin to the waves. Lane
+// (col, half) of a wave fetches half of the K row and half of the V row of key key0 + col: the K
+// half is directly its MFMA A fragment, the V half is transposed through a wave-private LDS tile.
+// The next block's fetch is issued before the current block's math (register double buffer).
+// A wave keeps an online softmax per column (no sink here), then the waves of the workgroup
+// merge through LDS in a fixed order:
 //   * single pass (one split): the sink joins the merge and O / LSE are written;
 //   * several splits: the merged, unnormalised (m, l, acc) go to the workspace and
 //     combine_kernel folds the splits and the sink (counted once) into O / LSE.
+// Keys past the end of the split are fetched from its last key (finite data, masked to weight 0).
 #include "launch.hpp"
 
 namespace mimo {
 
 constexpr int kDDQK = 192;
 constexpr int kDDV = 128;
-constexpr int kDecNW = 4;      // waves per workgroup
+constexpr int kDecNW = 4;  // waves per workgroup
 
 template <typename E, int NCB>
 struct DecodeLds {
@@ -37,19 +42,63 @@ struct DecodeLds {
   static constexpr int kBytes = kQBytes + kWorkBytes + kDecNW * 64 * 4 * 2;
 };
 
-// Address of key row `pos` (logical position) of sequence b / KV head g.
-__device__ __forceinline__ const char* key_row(const char* cache, const char* fresh, size_t row_bytes,
-                                               int Hkv, int C, int T, int b, int g, int P, int off,
-                                               int pos) {
-  if (pos < P) {
-    long long slot = ((long long)pos + off) % C;
-    if (slot < 0) slot += C;
-    return cache + (((size_t)b * C + (size_t)slot) * Hkv + g) * row_bytes;
-  }
-  return fresh + (((size_t)b * T + (size_t)(pos - P)) * Hkv + g) * row_bytes;
-}
+// One lane's share of a 32-key block: half of the K row (its MFMA A fragments) and half of the V
+// row (dv chunks 2i + half) of key key0 + col.
+template <typename E>
+struct KeyRows {
+  static constexpr int kKChunks = kDDQK / E::kPerChunk / 2;  // 16-byte chunks per lane
+  static constexpr int kVChunks = kDDV / E::kPerChunk / 2;
+  u32x4 k[kKChunks];
+  u32x4 v[kVChunks];
 
-template <typename E, int NCB>
+  __device__ __forceinline__ void load(const char* krow, const char* vrow, int half) {
+    // K chunk j: elements 8*(2*(j / (8/kPerChunk... ))) - laid out so that fragment kk of this
+    // half is chunk(s) of bytes [(16*kk + 8*half) * bytes, +8 elements)
+#pragma unroll
+    for (int j = 0; j < kKChunks; ++j) {
+      const int kk = j / (8 / E::kPerChunk);
+      const int sub = j % (8 / E::kPerChunk);
+      k[j] = ld16(krow + (16 * kk + 8 * half) * E::kBytes + 16 * sub);
+    }
+#pragma unroll
+    for (int i = 0; i < kVChunks; ++i) v[i] = ld16(vrow + (2 * i + half) * 16);
+  }
+
+  __device__ __forceinline__ typename E::Frag kfrag(int kk) const {
+    if constexpr (E::kBytes == 2) {
+      return __builtin_bit_cast(bf16x8, k[kk]);
+    } else {
+      f32x8 f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[i] = __uint_as_float(k[2 * kk][i]);
+        f[4 + i] = __uint_as_float(k[2 * kk + 1][i]);
+      }
+      return f;
+    }
+  }
+
+  // V^T[dv][key] <- this lane's V chunks (key = col); lanes of a half cover 32 consecutive keys.
+  __device__ __forceinline__ void store_vt(char* vt, int col, int half) const {
+    constexpr int S = DecodeLds<E, 1>::kVStride;
+#pragma unroll
+    for (int i = 0; i < kVChunks; ++i) {
+      const int dv0 = (2 * i + half) * E::kPerChunk;
+      if constexpr (E::kBytes == 2) {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(vt) + dv0 * S + col;
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+          dst[d * S] = (uint16_t)((d & 1) ? (v[i][d / 2] >> 16) : (v[i][d / 2] & 0xFFFFu));
+      } else {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(vt) + dv0 * S + col;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) dst[d * S] = v[i][d];
+      }
+    }
+  }
+};
+
+template <typename E, int NCB, bool PREFETCH>
 __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a) {
   using Frag = typename E::Frag;
   using Lds = DecodeLds<E, NCB>;
@@ -75,6 +124,14 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
 
   const size_t krow_bytes = (size_t)kDDQK * E::kBytes;
   const size_t vrow_bytes = (size_t)kDDV * E::kBytes;
+  const char* kc = (const char*)a.k_cache + (size_t)g * krow_bytes;
+  const char* vc = (const char*)a.v_cache + (size_t)g * vrow_bytes;
+  const char* kn = (const char*)a.k_new + (size_t)g * krow_bytes;
+  const char* vn = (const char*)a.v_new + (size_t)g * vrow_bytes;
+  const size_t kstride = (size_t)a.Hkv * krow_bytes;  // between positions
+  const size_t vstride = (size_t)a.Hkv * vrow_bytes;
+  const size_t cache_row0 = (size_t)b * a.C;
+  const size_t new_row0 = (size_t)b * a.T;
 
   // Q^T of every query column (head j of the group x new token t, column c = j * T + t) -> LDS.
   char* sq = smem;
@@ -102,96 +159,71 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
 #pragma unroll
     for (int db = 0; db < kDDV / 32; ++db) acc[cb][db] = zero16();
   }
-  __syncthreads();
+
+  // K and V row addresses of this lane's key in the block starting at key0 (clamped into the split)
+  auto rows = [&](int key0, const char*& krow, const char*& vrow) {
+    const int pos = min(key0 + col, s1 - 1);
+    if (pos < P) {
+      int slot = (pos + off) % a.C;
+      slot += slot < 0 ? a.C : 0;
+      krow = kc + (cache_row0 + slot) * kstride;
+      vrow = vc + (cache_row0 + slot) * vstride;
+    } else {
+      krow = kn + (new_row0 + (pos - P)) * kstride;
+      vrow = vn + (new_row0 + (pos - P)) * vstride;
+    }
+  };
 
   char* work = smem + Lds::kQBytes;
   char* my_vt = work + wave * Lds::kVBytes;
-  for (int key0 = s0 + 32 * wave; key0 < s1; key0 += 32 * kDecNW) {
-    // V block -> LDS, transposed to [dv][key]; unit = 4 keys x one 16-byte dv chunk.
-    constexpr int kVChunksRow = kDDV / E::kPerChunk;
-    constexpr int kUnits = 8 * kVChunksRow;
-#pragma unroll
-    for (int i = 0; i < kUnits / 64; ++i) {
-      const int u = lane + 64 * i;
-      const int kg = u / kVChunksRow, dc = u % kVChunksRow;
-      u32x4 vr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = key0 + 4 * kg + r;
-        vr[r] = zero_chunk();
-        if (pos < s1)
-          vr[r] = ld16(key_row((const char*)a.v_cache, (const char*)a.v_new, vrow_bytes, a.Hkv, a.C,
-                               a.T, b, g, P, off, pos) + dc * 16);
-      }
-      if constexpr (E::kBytes == 2) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          uint32_t e[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) e[r] = (d & 1) ? (vr[r][d / 2] >> 16) : (vr[r][d / 2] & 0xFFFFu);
-          u32x2 w;
-          w[0] = e[0] | (e[1] << 16);
-          w[1] = e[2] | (e[3] << 16);
-          *reinterpret_cast<u32x2*>(my_vt + ((dc * 8 + d) * Lds::kVStride + 4 * kg) * 2) = w;
-        }
-      } else {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          u32x4 w;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) w[r] = vr[r][d];
-          st16(my_vt + ((dc * 4 + d) * Lds::kVStride + 4 * kg) * 4, w);
-        }
-      }
+  KeyRows<E> cur;
+  int key0 = s0 + 32 * wave;
+  if (key0 < s1) {
+    const char *kr, *vr;
+    rows(key0, kr, vr);
+    cur.load(kr, vr, half);
+  }
+  __syncthreads();  // Q^T is in LDS
+
+  for (; key0 < s1; key0 += 32 * kDecNW) {
+    cur.store_vt(my_vt, col, half);
+    KeyRows<E> nxt;
+    const int key_next = key0 + 32 * kDecNW;
+    if (PREFETCH && key_next < s1) {
+      const char *kr, *vr;
+      rows(key_next, kr, vr);
+      nxt.load(kr, vr, half);
     }
 
-    // S^T = K Q^T: K rows come straight from memory as A fragments (key = key0 + col).
+    // S^T = K Q^T for every column block
     f32x16 s[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) s[cb] = zero16();
-    {
-      const int pos = key0 + col;
-      const bool kvalid = pos < s1;
-      const char* krow = kvalid ? key_row((const char*)a.k_cache, (const char*)a.k_new, krow_bytes,
-                                          a.Hkv, a.C, a.T, b, g, P, off, pos)
-                                : (const char*)a.k_new;
 #pragma unroll
-      for (int kk = 0; kk < kDDQK / 16; ++kk) {
-        const char* p = krow + (16 * kk + 8 * half) * E::kBytes;
-        Frag kf;
+    for (int kk = 0; kk < kDDQK / 16; ++kk) {
+      const Frag kf = cur.kfrag(kk);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const char* qp = sq + ((cb * 32 + col) * Lds::kQStride + 16 * kk + 8 * half) * E::kBytes;
+        Frag qf;
         if constexpr (E::kBytes == 2) {
-          kf = __builtin_bit_cast(bf16x8, kvalid ? ld16(p) : zero_chunk());
+          qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp));
         } else {
-          const u32x4 x = kvalid ? ld16(p) : zero_chunk();
-          const u32x4 y = kvalid ? ld16(p + 16) : zero_chunk();
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            kf[i] = __uint_as_float(x[i]);
-            kf[4 + i] = __uint_as_float(y[i]);
-          }
+          const f32x4 x = *reinterpret_cast<const f32x4*>(qp);
+          const f32x4 y = *reinterpret_cast<const f32x4*>(qp + 16);
+          qf[0] = x[0]; qf[1] = x[1]; qf[2] = x[2]; qf[3] = x[3];
+          qf[4] = y[0]; qf[5] = y[1]; qf[6] = y[2]; qf[7] = y[3];
         }
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const char* qp = sq + ((cb * 32 + col) * Lds::kQStride + 16 * kk + 8 * half) * E::kBytes;
-          Frag qf;
-          if constexpr (E::kBytes == 2) {
-            qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp));
-          } else {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(qp);
-            const f32x4 y = *reinterpret_cast<const f32x4*>(qp + 16);
-            qf[0] = x[0]; qf[1] = x[1]; qf[2] = x[2]; qf[3] = x[3];
-            qf[4] = y[0]; qf[5] = y[1]; qf[6] = y[2]; qf[7] = y[3];
-          }
-          s[cb] = mma(kf, qf, s[cb]);
-        }
+        s[cb] = mma(kf, qf, s[cb]);
       }
     }
 
-    // The V^T block was written by other lanes of this wave: order those writes before the reads.
+    // V^T was written by other lanes of this wave: order those writes before the reads below
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+    const float c = a.scale_log2;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       float bmax = -INFINITY;
@@ -199,28 +231,29 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
       for (int r = 0; r < 16; ++r) {
         const int pos = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
         const int d = qpos[cb] - pos;
-        const float t = (d >= 0 && d < a.window && pos < s1) ? s[cb][r] * a.scale_log2 : -INFINITY;
-        s[cb][r] = t;
-        bmax = fmaxf(bmax, t);
+        s[cb][r] = (d >= 0 && d < a.window && pos < s1) ? s[cb][r] : -INFINITY;
+        bmax = fmaxf(bmax, s[cb][r]);
       }
-      bmax = halves_max(bmax);
+      bmax = halves_max(bmax) * c;
       const float m_new = fmaxf(m[cb], bmax);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = fast_exp2(m[cb] - m_use);
       float rs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(s[cb][r] - m_use);
+        const float p = fast_exp2(__builtin_fmaf(s[cb][r], c, -m_use));
         s[cb][r] = p;
         rs += p;
       }
       rs = halves_sum(rs);
       l[cb] = l[cb] * alpha + rs;
       m[cb] = m_new;
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int db = 0; db < kDDV / 32; ++db)
+        for (int db = 0; db < kDDV / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[cb][db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) acc[cb][db][r] *= alpha;
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const Frag pf = frag_from_acc<E>(s[cb], 8 * ks);
@@ -244,10 +277,18 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
         }
       }
     }
-    // The next block rewrites this wave's V^T buffer: finish every read of it first.
+    // the next block rewrites this wave's V^T tile: finish every read of it first
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    if (PREFETCH) {
+      cur = nxt;
+    } else if (key_next < s1) {
+      const char *kr, *vr;
+      rows(key_next, kr, vr);
+      cur.load(kr, vr, half);
+    }
   }
 
   // ---- merge the waves of this workgroup, one column block at a time (fixed order) ----
@@ -274,12 +315,13 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
 #pragma unroll
     for (int db = 0; db < kDDV / 32; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sm_acc[((wave * (kDDV / 32) + db) * 16 + r) * 64 + lane] = acc[cb][db][r] * scale_w;
+      for (int r = 0; r < 16; ++r)
+        sm_acc[((wave * (kDDV / 32) + db) * 16 + r) * 64 + lane] = acc[cb][db][r] * scale_w;
     sm_l[wave * 64 + lane] = l[cb] * scale_w;
     __syncthreads();
-    float L = fold_sink ? fast_exp2(s_l2 - M_use) : 0.f;
+    float Lsum = fold_sink ? fast_exp2(s_l2 - M_use) : 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecNW; ++w) L += sm_l[w * 64 + lane];
+    for (int w = 0; w < kDecNW; ++w) Lsum += sm_l[w * 64 + lane];
     // wave w reduces dv block db = w (kDecNW == kDDV / 32)
     const int db = wave;
     f32x16 o = zero16();
@@ -288,7 +330,7 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[r] += sm_acc[((w * (kDDV / 32) + db) * 16 + r) * 64 + lane];
     if (cvalid && a.nsplit == 1) {
-      const float inv = 1.f / L;
+      const float inv = 1.f / Lsum;
       char* orow = (char*)a.o + (((size_t)b * a.T + t) * a.Hq + head) * kDDV * E::kBytes;
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
@@ -307,22 +349,22 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
         }
       }
       if (a.lse && wave == 0 && half == 0)
-        a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(L)) * kLn2;
+        a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(Lsum)) * kLn2;
     } else if (cvalid) {
       // partial record for (b, g, split, column c): acc[kDDV], m, l
       const int ncols_pad = NCB * 32;
       float* rec = a.ws + ((((size_t)b * a.Hkv + g) * a.nsplit + split) * ncols_pad + c) * (kDDV + 2);
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int dv = 32 * db + 8 * gq + 4 * half;
-        f32x4 w;
-        w[0] = o[4 * gq]; w[1] = o[4 * gq + 1]; w[2] = o[4 * gq + 2]; w[3] = o[4 * gq + 3];
-        float* dst = rec + dv;  // records are only 8-byte aligned (kDDV + 2 floats each)
-        dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2]; dst[3] = w[3];
+        float* dst = rec + 32 * db + 8 * gq + 4 * half;  // records are only 8-byte aligned
+        dst[0] = o[4 * gq];
+        dst[1] = o[4 * gq + 1];
+        dst[2] = o[4 * gq + 2];
+        dst[3] = o[4 * gq + 3];
       }
       if (wave == 0 && half == 0) {
         rec[kDDV] = M;
-        rec[kDDV + 1] = L;
+        rec[kDDV + 1] = Lsum;
       }
     }
   }
@@ -369,18 +411,24 @@ size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit) {
   return (size_t)B * Hkv * nsplit * ncols_pad * (kDDV + 2) * sizeof(float);
 }
 
+// With one column block (e.g. 8 query heads x 4 tokens) a wave holds few blocks and fewer
+// registers buy a second wave per SIMD; that beats prefetching (measured on the ring workload).
+#ifndef MIMO_DECODE_PREFETCH_1COL
+#define MIMO_DECODE_PREFETCH_1COL false
+#endif
+
 hipError_t decode_launch(bool bf16, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
   const dim3 block(kDecNW * 64);
   const bool two = a.ncols > 32;
   if (bf16 && two)
-    hipLaunchKernelGGL((decode_kernel<BF16, 2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<BF16, 2, true>), grid, block, 0, stream, a);
   else if (bf16)
-    hipLaunchKernelGGL((decode_kernel<BF16, 1>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<BF16, 1, MIMO_DECODE_PREFETCH_1COL>), grid, block, 0, stream, a);
   else if (two)
-    hipLaunchKernelGGL((decode_kernel<F32, 2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<F32, 2, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<F32, 1>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<F32, 1, false>), grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const dim3 cgrid(a.ncols, a.Hkv, a.B);

@@ -21,6 +21,8 @@ struct PrefillArgs {
   int heads_per_wg;  // HG
   int n_qblocks;     // ceil(L / (32 * NW / HG))
   int n_hchunks;     // G / HG
+  int n_segments;    // sliding-window ring kernel: segments of consecutive tiles per (b, g, chunk)
+  int tiles_per_wg;  // sliding-window ring kernel: 32-row tiles per segment
   HeadList hl;
 };
 

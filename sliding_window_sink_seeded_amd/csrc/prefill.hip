@@ -1,22 +1,29 @@
-// Prefill kernel: sink-seeded sliding-window / causal attention on gfx950 MFMA.
+// Prefill kernels: sink-seeded sliding-window / causal attention on gfx950 MFMA.
 //
 // Operation: MiMo-V2-Flash Technical Report review (xllm-io), §3.1 (window 128, GQA 64/8 and 64/4,
 // head dims 192/128) and §3.2 (per-head sink logit in the softmax denominator); MiMo series notes
 // (plmsmile), MiMo-V2-Flash > Learnable Attention Sink > mechanism (real-token weights may sum to
 // less than one; the sink carries no value).
 //
-// Work decomposition (one workgroup = NW waves):
-//   * A workgroup owns one KV head g of one sequence b, HG query heads of that group and
-//     NW / HG tiles of 32 consecutive query positions. Every K/V block it stages in LDS is read
-//     from HBM/L2 once and consumed by all of its waves, i.e. by every query head sharing g.
-//   * Wave w owns query head (w % HG) and query tile (w / HG): 32 positions = 32 MFMA columns.
-//   * The key loop covers only the union of the workgroup's windows, [P0 - W + 1, P1), in blocks
-//     of BK keys, double-buffered in LDS; a block is skipped by a wave whose queries see none of it
-//     and masked only when some (query, key) pair inside it is invisible.
-//   * Scores are formed transposed, S^T = K Q^T, so that each lane holds one query column: row
-//     max/sum need one cross-half exchange, and P^T feeds O^T += V^T P^T straight from registers.
-//   * The online softmax starts from the sink: m = s_h * log2(e), l = 1, acc = 0 (no sink:
-//     m = -inf, l = 0), so the sink is counted exactly once and never multiplied by the scale.
+// Shared structure:
+//   * A workgroup owns one KV head g of one sequence b and a group of query heads of g, so every
+//     K/V block it stages in LDS serves all of those heads (GQA reuse).
+//   * Wave w owns one query head and a tile of 32 consecutive query positions = 32 MFMA columns.
+//   * Scores are formed transposed, S^T = K Q^T, so each lane holds one query column: row max and
+//     sum need one cross-half exchange, and P^T feeds O^T += V^T P^T straight from registers.
+//   * The softmax starts from the sink, m = s_h * log2(e), l = 1 (no sink: m = -inf, l = 0), so
+//     the sink is counted once and is never multiplied by the scale. Scores are scaled inside the
+//     exponent: p = exp2(s * scale * log2(e) - m), which needs scale > 0 (checked by the host).
+//   * Rows or keys past the end of the sequence are read from clamped, valid addresses: their
+//     scores are masked to -inf, so they get weight exactly 0 and touch no output.
+//
+// prefill_swa_kernel (bf16, window <= 129, query heads per KV head a multiple of 8): a workgroup
+//   walks a segment of consecutive 32-position tiles. The window of a tile is NB 32-key blocks;
+//   they sit in an LDS ring of NB + 1 slots, so each K/V row is fetched once per segment and only
+//   the next tile's diagonal block is loaded per step (prefetched under the current tile's math).
+//   The whole window is scored before the softmax, so it is single pass (no rescaling).
+// prefill_kernel (generic: global attention, fp32, other shapes): streams the union of the
+//   workgroup's windows in BK-key blocks, double-buffered in LDS, with an online softmax.
 #include "launch.hpp"
 
 namespace mimo {
@@ -36,41 +43,38 @@ struct PrefillTile {
 };
 
 // Global -> register -> LDS staging of one K block (row-major) and one V block (transposed).
+// K: consecutive threads take consecutive 16-byte chunks of a row (coalesced loads and stores).
+// V: thread chunk c holds key c % BK and dv chunk c / BK, so the lanes of a wave cover 32 or 64
+// consecutive keys of one dv range and their 2- or 4-byte transposed LDS writes hit distinct banks.
+// Keys at or past L are read from row L - 1 (finite data that the mask gives weight 0).
 template <typename E, int NT, int BK>
 struct KVStager {
   using Tile = PrefillTile<E, BK>;
   static constexpr int kKChunksRow = kDQK / E::kPerChunk;
   static constexpr int kKChunks = BK * kKChunksRow;
   static constexpr int kKIt = (kKChunks + NT - 1) / NT;
-  static constexpr int kVChunksRow = kDV / E::kPerChunk;
-  static constexpr int kVUnits = (BK / 4) * kVChunksRow;  // unit = 4 keys x one 16-byte dv chunk
-  static constexpr int kVIt = (kVUnits + NT - 1) / NT;
+  static constexpr int kVChunks = BK * (kDV / E::kPerChunk);
+  static constexpr int kVIt = (kVChunks + NT - 1) / NT;
 
   u32x4 kr[kKIt];
-  u32x4 vr[kVIt][4];
+  u32x4 vr[kVIt];
 
   __device__ __forceinline__ void load(const char* kbase, const char* vbase, size_t kstride,
                                        size_t vstride, int key0, int L, int tid) {
 #pragma unroll
     for (int i = 0; i < kKIt; ++i) {
       const int c = tid + i * NT;
-      kr[i] = zero_chunk();
-      if (c < kKChunks) {
-        const int key = key0 + c / kKChunksRow;
-        if (key < L) kr[i] = ld16(kbase + (size_t)key * kstride + (c % kKChunksRow) * 16);
+      if (kKChunks % NT == 0 || c < kKChunks) {
+        const int key = min(key0 + c / kKChunksRow, L - 1);
+        kr[i] = ld16(kbase + (size_t)key * kstride + (c % kKChunksRow) * 16);
       }
     }
 #pragma unroll
     for (int i = 0; i < kVIt; ++i) {
-      const int u = tid + i * NT;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vr[i][r] = zero_chunk();
-      if (u < kVUnits) {
-        const int key = key0 + 4 * (u / kVChunksRow);
-        const size_t col = (size_t)(u % kVChunksRow) * 16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (key + r < L) vr[i][r] = ld16(vbase + (size_t)(key + r) * vstride + col);
+      const int c = tid + i * NT;
+      if (kVChunks % NT == 0 || c < kVChunks) {
+        const int key = min(key0 + c % BK, L - 1);
+        vr[i] = ld16(vbase + (size_t)key * vstride + (c / BK) * 16);
       }
     }
   }
@@ -81,35 +85,24 @@ struct KVStager {
 #pragma unroll
     for (int i = 0; i < kKIt; ++i) {
       const int c = tid + i * NT;
-      if (c < kKChunks)
+      if (kKChunks % NT == 0 || c < kKChunks)
         st16(sk + ((c / kKChunksRow) * Tile::kKStride) * E::kBytes + (c % kKChunksRow) * 16, kr[i]);
     }
 #pragma unroll
     for (int i = 0; i < kVIt; ++i) {
-      const int u = tid + i * NT;
-      if (u >= kVUnits) continue;
-      const int kg = u / kVChunksRow;  // keys 4kg .. 4kg+3 of the block
-      const int dc = u % kVChunksRow;  // dv elements dc*kPerChunk ..
+      const int c = tid + i * NT;
+      if (!(kVChunks % NT == 0 || c < kVChunks)) continue;
+      const int key = c % BK;
+      const int dv0 = (c / BK) * E::kPerChunk;
       if constexpr (E::kBytes == 2) {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(sv) + dv0 * Tile::kVStride + key;
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          const int w = d / 2;
-          uint32_t e[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) e[r] = (d & 1) ? (vr[i][r][w] >> 16) : (vr[i][r][w] & 0xFFFFu);
-          u32x2 out;
-          out[0] = e[0] | (e[1] << 16);
-          out[1] = e[2] | (e[3] << 16);
-          *reinterpret_cast<u32x2*>(sv + ((dc * 8 + d) * Tile::kVStride + 4 * kg) * 2) = out;
-        }
+        for (int d = 0; d < 8; ++d)
+          dst[d * Tile::kVStride] = (uint16_t)((d & 1) ? (vr[i][d / 2] >> 16) : (vr[i][d / 2] & 0xFFFFu));
       } else {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(sv) + dv0 * Tile::kVStride + key;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          u32x4 out;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) out[r] = vr[i][r][d];
-          st16(sv + ((dc * 4 + d) * Tile::kVStride + 4 * kg) * 4, out);
-        }
+        for (int d = 0; d < 4; ++d) dst[d * Tile::kVStride] = vr[i][d];
       }
     }
   }
@@ -152,17 +145,15 @@ __device__ __forceinline__ typename E::Frag lds_vt_frag(const char* sv, int row,
   }
 }
 
-// B-operand fragment of Q^T straight from global memory: this lane's query row, elements
-// 16*kk + 8*half .. +7 (zero for rows past the end of the sequence).
+// B-operand fragment of Q^T from global memory: elements 16*kk + 8*half .. +7 of a query row.
 template <typename E>
-__device__ __forceinline__ typename E::Frag global_q_frag(const char* qrow, bool valid, int kk,
-                                                          int half) {
+__device__ __forceinline__ typename E::Frag global_q_frag(const char* qrow, int kk, int half) {
   const char* p = qrow + (16 * kk + 8 * half) * E::kBytes;
   if constexpr (E::kBytes == 2) {
-    return __builtin_bit_cast(bf16x8, valid ? ld16(p) : zero_chunk());
+    return __builtin_bit_cast(bf16x8, ld16(p));
   } else {
-    const u32x4 a = valid ? ld16(p) : zero_chunk();
-    const u32x4 b = valid ? ld16(p + 16) : zero_chunk();
+    const u32x4 a = ld16(p);
+    const u32x4 b = ld16(p + 16);
     f32x8 f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -172,6 +163,29 @@ __device__ __forceinline__ typename E::Frag global_q_frag(const char* qrow, bool
     return f;
   }
 }
+
+// Writes one output row from O^T registers; every lane calls it, lanes with !store write nothing.
+template <typename E>
+__device__ __forceinline__ void store_out_row(char* orow, const f32x16 (&acc)[kDV / 32], float inv,
+                                              int half, bool store) {
+  if constexpr (E::kBytes == 2) {
+    store_row_bf16(orow, acc, inv, half, store);
+  } else {
+    if (!store) return;
+#pragma unroll
+    for (int db = 0; db < kDV / 32; ++db) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        f32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = acc[db][4 * gq + i] * inv;
+        *reinterpret_cast<f32x4*>(orow + (32 * db + 8 * gq + 4 * half) * 4) = w;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------ generic streaming kernel
 
 template <typename E, int NW, int BK>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
@@ -209,16 +223,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   const char* kbase = (const char*)a.k + ((size_t)b * a.L * a.Hkv + g) * kDQK * E::kBytes;
   const char* vbase = (const char*)a.v + ((size_t)b * a.L * a.Hkv + g) * kDV * E::kBytes;
 
-  // Q^T fragments for the whole key loop.
   Frag qf[kDQK / 16];
   {
-    const char* qrow = (const char*)a.q + (((size_t)b * a.L + qpos) * a.Hq + head) * kDQK * E::kBytes;
-    const bool valid = qpos < a.L;
+    const int qload = min(qpos, a.L - 1);
+    const char* qrow = (const char*)a.q + (((size_t)b * a.L + qload) * a.Hq + head) * kDQK * E::kBytes;
 #pragma unroll
-    for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, valid, kk, half);
+    for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
   }
 
-  // Sink-seeded softmax state of this lane's query (identical in both lane halves).
+  const float c = a.scale_log2;
   const float sink_l2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
   float m = sink_l2;
   float l = a.sink ? 1.f : 0.f;
@@ -233,6 +246,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   KVStager<E, NT, BK> st;
   st.load(kbase, vbase, krow_stride, vrow_stride, kstart, a.L, tid);
   st.store(smem, tid);
+  wait_all();
   __syncthreads();
 
   for (int ib = 0; ib < nblk; ++ib) {
@@ -247,29 +261,27 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
 
       f32x16 s[NSB];
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
-        s[sb] = zero16();
+      for (int sb = 0; sb < NSB; ++sb) s[sb] = zero16();
 #pragma unroll
-        for (int kk = 0; kk < kDQK / 16; ++kk)
+      for (int kk = 0; kk < kDQK / 16; ++kk)
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
           s[sb] = mma(lds_k_frag<E, BK>(sk, 32 * sb + col, kk, half), qf[kk], s[sb]);
-      }
 
       float bmax = -INFINITY;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float t = s[sb][r] * a.scale_log2;
           if (need_mask) {
             const int key = key0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
             const int d = qpos - key;
-            t = (d >= 0 && d < a.window) ? t : -INFINITY;
+            s[sb][r] = (d >= 0 && d < a.window) ? s[sb][r] : -INFINITY;
           }
-          s[sb][r] = t;
-          bmax = fmaxf(bmax, t);
+          bmax = fmaxf(bmax, s[sb][r]);
         }
       }
-      bmax = halves_max(bmax);
+      bmax = halves_max(bmax) * c;
       const float m_new = fmaxf(m, bmax);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = fast_exp2(m - m_use);
@@ -278,7 +290,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
       for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(s[sb][r] - m_use);
+          const float p = fast_exp2(__builtin_fmaf(s[sb][r], c, -m_use));
           s[sb][r] = p;
           rs += p;
         }
@@ -306,30 +318,167 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
     __syncthreads();
   }
 
-  if (qpos < a.L) {
-    const float inv = 1.f / l;
-    char* orow = (char*)a.o + (((size_t)b * a.L + qpos) * a.Hq + head) * kDV * E::kBytes;
+  const bool valid = qpos < a.L;
+  char* orow = (char*)a.o + (((size_t)b * a.L + min(qpos, a.L - 1)) * a.Hq + head) * kDV * E::kBytes;
+  store_out_row<E>(orow, acc, 1.f / l, half, valid);
+  if (a.lse && half == 0 && valid)
+    a.lse[((size_t)b * a.Hq + head) * a.L + qpos] = (m + fast_log2(l)) * kLn2;
+}
+
+// ---------------------------------------------------------------- sliding-window ring kernel
+
+template <int NB>
+__global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
+  using E = BF16;
+  using Tile = PrefillTile<E, 32>;
+  constexpr int NW = 8, NT = 512, R = NB + 1;
+  __shared__ __attribute__((aligned(16))) char smem[R * Tile::kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int wave = tid >> 6;
+
+  // workgroup -> (segment, head chunk, KV head, sequence); segments of one (b, g) are adjacent
+  int rest = blockIdx.x;
+  const int seg = rest % a.n_segments;
+  rest /= a.n_segments;
+  const int hc = rest % a.n_hchunks;
+  rest /= a.n_hchunks;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  const int head = a.hl.heads[g * a.G + hc * NW + wave];
+
+  const int n_tiles = (a.L + kQT - 1) / kQT;
+  const int t0 = seg * a.tiles_per_wg;
+  const int t1 = min(n_tiles, t0 + a.tiles_per_wg);
+
+  const size_t krow_stride = (size_t)a.Hkv * kDQK * 2;
+  const size_t vrow_stride = (size_t)a.Hkv * kDV * 2;
+  const size_t qrow_stride = (size_t)a.Hq * kDQK * 2;
+  const size_t orow_stride = (size_t)a.Hq * kDV * 2;
+  const char* kbase = (const char*)a.k + ((size_t)b * a.L * a.Hkv + g) * kDQK * 2;
+  const char* vbase = (const char*)a.v + ((size_t)b * a.L * a.Hkv + g) * kDV * 2;
+  const char* qbase = (const char*)a.q + ((size_t)b * a.L * a.Hq + head) * kDQK * 2;
+  char* obase = (char*)a.o + ((size_t)b * a.L * a.Hq + head) * kDV * 2;
+
+  const float c = a.scale_log2;
+  const float sink_l2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
+  const int W = a.window;
+
+  // ring slot of key block kb (kb >= -NB + 1)
+  auto slot = [](int kb) { return (kb + R) % R; };
+
+  // prologue: zero the slots of blocks before position 0 (they are scored, masked, and must hold
+  // finite values), then stage the window of tile t0 (blocks t0 - NB + 1 .. t0) and Q of tile t0
+  if (t0 < NB - 1) {
+    for (int i = tid; i < R * Tile::kStageBytes / 16; i += NT) st16(smem + 16 * i, zero_chunk());
+    __syncthreads();
+  }
+  {
+    KVStager<E, NT, 32> pro[NB];
 #pragma unroll
-    for (int db = 0; db < kDV / 32; ++db) {
+    for (int j = 0; j < NB; ++j)
+      if (t0 - NB + 1 + j >= 0)
+        pro[j].load(kbase, vbase, krow_stride, vrow_stride, 32 * (t0 - NB + 1 + j), a.L, tid);
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int dv = 32 * db + 8 * gq + 4 * half;
-        const float x0 = acc[db][4 * gq + 0] * inv, x1 = acc[db][4 * gq + 1] * inv;
-        const float x2 = acc[db][4 * gq + 2] * inv, x3 = acc[db][4 * gq + 3] * inv;
-        if constexpr (E::kBytes == 2) {
-          u32x2 w;
-          w[0] = pack_bf16x2(x0, x1);
-          w[1] = pack_bf16x2(x2, x3);
-          *reinterpret_cast<u32x2*>(orow + dv * 2) = w;
-        } else {
-          f32x4 w;
-          w[0] = x0; w[1] = x1; w[2] = x2; w[3] = x3;
-          *reinterpret_cast<f32x4*>(orow + dv * 4) = w;
+    for (int j = 0; j < NB; ++j)
+      if (t0 - NB + 1 + j >= 0) pro[j].store(smem + slot(t0 - NB + 1 + j) * Tile::kStageBytes, tid);
+  }
+  bf16x8 qf[kDQK / 16];
+  {
+    const char* qrow = qbase + (size_t)min(kQT * t0 + col, a.L - 1) * qrow_stride;
+#pragma unroll
+    for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
+  }
+  wait_all();
+  __syncthreads();
+
+  KVStager<E, NT, 32> st;
+  for (int t = t0; t < t1; ++t) {
+    const int p0 = kQT * t;
+    const int qpos = p0 + col;
+    const bool has_next = t + 1 < t1;
+    int base[NB];  // byte offset of each window block's ring slot
+#pragma unroll
+    for (int j = 0; j < NB; ++j) base[j] = slot(t - NB + 1 + j) * Tile::kStageBytes;
+
+    // scores of the whole window: block j holds keys 32 * (t - NB + 1 + j) ..
+    f32x16 s[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) s[j] = zero16();
+#pragma unroll
+    for (int kk = 0; kk < kDQK / 16; ++kk)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) s[j] = mma(lds_k_frag<E, 32>(smem + base[j], col, kk, half), qf[kk], s[j]);
+
+    // the next tile's Q and diagonal K/V block stream in under this tile's softmax and P.V
+    if (has_next) {
+      const char* qrow = qbase + (size_t)min(qpos + kQT, a.L - 1) * qrow_stride;
+#pragma unroll
+      for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
+      st.load(kbase, vbase, krow_stride, vrow_stride, 32 * (t + 1), a.L, tid);
+    }
+
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int kb = t - NB + 1 + j;
+      // masked: future keys (diagonal block), keys older than the window, keys before 0
+      const bool need_mask = (j == NB - 1) || (kb < 0) || (32 * kb <= p0 + kQT - 1 - W);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int d = qpos - key;
+          s[j][r] = (key >= 0 && d >= 0 && d < W) ? s[j][r] : -INFINITY;
         }
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[j][r]);
     }
-    if (a.lse && half == 0)
-      a.lse[((size_t)b * a.Hq + head) * a.L + qpos] = (m + fast_log2(l)) * kLn2;
+    const float m = fmaxf(sink_l2, halves_max(rmax) * c);
+    const float m_use = (m == -INFINITY) ? 0.f : m;
+
+    // probabilities go straight to bf16 MFMA fragments (half the registers of fp32 scores)
+    float l = 0.f;
+    bf16x8 pf[NB][2];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[j][r], c, -m_use));
+        s[j][r] = p;
+        l += p;
+      }
+      pf[j][0] = frag_from_acc<E>(s[j], 0);
+      pf[j][1] = frag_from_acc<E>(s[j], 8);
+    }
+    l = halves_sum(l) + (a.sink ? fast_exp2(sink_l2 - m_use) : 0.f);
+
+    f32x16 acc[kDV / 32];
+#pragma unroll
+    for (int db = 0; db < kDV / 32; ++db) acc[db] = zero16();
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < kDV / 32; ++db)
+          acc[db] = mma(lds_vt_frag<E, 32>(smem + base[j] + Tile::kKBytes, 32 * db + col, ks, half),
+                        pf[j][ks], acc[db]);
+
+    // ring update first, output stores last: the stores drain under the barrier and the next
+    // tile's score MFMAs instead of holding up the loads that reuse their registers
+    u32x4 out[8];
+    pack_row_bf16(acc, 1.f / l, out);
+    if (has_next) st.store(smem + slot(t + 1) * Tile::kStageBytes, tid);
+    if (qpos < a.L) {
+      store_packed_row_bf16(obase + (size_t)qpos * orow_stride, out, half);
+      if (a.lse && half == 0) a.lse[((size_t)b * a.Hq + head) * a.L + qpos] = (m + fast_log2(l)) * kLn2;
+    }
+    __syncthreads();
   }
 }
 
@@ -338,6 +487,31 @@ static hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const long long n_wg = (long long)a.n_qblocks * a.B * a.Hkv * a.n_hchunks;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_kernel<E, NW, BK>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+#ifndef MIMO_SWA_WG_PER_CU
+#define MIMO_SWA_WG_PER_CU 4
+#endif
+#ifndef MIMO_SWA_MIN_TILES
+#define MIMO_SWA_MIN_TILES 8
+#endif
+
+template <int NB>
+static hipError_t launch_swa(PrefillArgs a, hipStream_t stream) {
+  const int n_tiles = (a.L + kQT - 1) / kQT;
+  const long long units = (long long)a.B * a.Hkv * a.n_hchunks;
+  // spread the tiles of every (b, g, head chunk) over segments so that about
+  // MIMO_SWA_WG_PER_CU workgroups per compute unit run in total
+  long long segs = (MIMO_SWA_WG_PER_CU * 256LL + units - 1) / units;
+  segs = segs < 1 ? 1 : segs;
+  long long per = (n_tiles + segs - 1) / segs;
+  if (per < MIMO_SWA_MIN_TILES) per = MIMO_SWA_MIN_TILES;
+  a.tiles_per_wg = (int)per;
+  a.n_segments = (int)((n_tiles + per - 1) / per);
+  const long long n_wg = units * a.n_segments;
+  if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_swa_kernel<NB>), dim3((unsigned)n_wg), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -352,6 +526,16 @@ hipError_t prefill_launch(bool bf16, PrefillArgs a, hipStream_t stream) {
   a.n_qblocks = (a.L + rows_per_wg - 1) / rows_per_wg;
   const bool global = a.window >= a.L;
   if (!bf16) return launch<F32, NW, 32>(a, stream);
+  if (!global && hg == NW && a.window <= 129) {
+    const int nb = (a.window - 1 + 31) / 32 + 1;  // 32-key blocks in a 32-row tile's window
+    switch (nb) {
+      case 1:
+      case 2: return launch_swa<2>(a, stream);
+      case 3: return launch_swa<3>(a, stream);
+      case 4: return launch_swa<4>(a, stream);
+      default: return launch_swa<5>(a, stream);
+    }
+  }
   if (global) return launch<BF16, NW, 64>(a, stream);
   return launch<BF16, NW, 32>(a, stream);
 }
