@@ -255,6 +255,10 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--warm-seconds", type=float, default=0.25,
+                    help="keep warming up (untimed) until this much time has passed")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -270,8 +274,18 @@ def main():
     torch.cuda.set_device(0)
     w = workloads.WORKLOADS[args.workload]
 
+    if args.calibrate_copy:
+        # a plain copy kernel of known size: reads 1 GiB and writes 1 GiB per launch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+
     case = Case(w)
-    wall_ms, event_ms = case.time(args.steps, args.warmup)
+    wall_ms, event_ms = case.time(args.steps, args.warmup, args.warm_seconds)
     head = describe(case, wall_ms, event_ms)
     log(f"[bench] {w.name}: {head}")
     parity = None if args.no_parity else case.sampled_parity()
@@ -299,7 +313,7 @@ def main():
             if name == w.name:
                 continue
             c = Case(workloads.WORKLOADS[name])
-            sw, se = c.time(max(5, args.steps // 2), 3)
+            sw, se = c.time(max(5, args.steps // 2), 3, args.warm_seconds)
             d = describe(c, sw, se)
             log(f"[bench] {name}: {d}")
             secondary.append(d)

@@ -164,6 +164,36 @@ __device__ __forceinline__ void store_row_bf16(char* orow, const f32x16 (&acc)[4
   if (store) store_packed_row_bf16(orow, out, half);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, output lane j element e is element
+// (j % 4) of the 8 bytes read by lane 4 e + j / 4. If lanes 4e..4e+3 of a group read four
+// consecutive 4-element pieces of row e of a row-major tile, every lane receives one column
+// (4 consecutive rows) of it.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(lds_ptr));
+}
+
+// A-operand fragment of V^T for O^T += V^T P^T, read from a row-major bf16 V tile
+// ([key][dv], row stride `row_elems`): this lane's dv row is 32 db + lane % 32 and its 8 elements
+// are keys 16 ks + 4 half + 0..3 and 16 ks + 8 + 4 half + 0..3 (the order in which the S^T
+// accumulator holds P for this lane half).
+__device__ __forceinline__ bf16x8 vt_frag_tr(const char* vtile, int row_elems, int db, int ks,
+                                             int lane) {
+  const int half = lane >> 5, i = lane & 15, dsub = (lane >> 4) & 1;
+  const int key = 16 * ks + 4 * half + (i >> 2);
+  const int dv = 32 * db + 16 * dsub + 4 * (i & 3);
+  const char* p = vtile + (key * row_elems + dv) * 2;
+  const s16x4 x = lds_read_tr16(p);
+  const s16x4 y = lds_read_tr16(p + 8 * row_elems * 2);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 u;
+  u[0] = x[0]; u[1] = x[1]; u[2] = x[2]; u[3] = x[3];
+  u[4] = y[0]; u[5] = y[1]; u[6] = y[2]; u[7] = y[3];
+  return __builtin_bit_cast(bf16x8, u);
+}
+
 // Query heads grouped by KV head: heads[g * G + j] is the j-th query head served by KV head g.
 struct HeadList {
   int16_t heads[kMaxHeads];

@@ -15,7 +15,8 @@
 // column block), so each K/V element read from HBM serves all of them; Q^T sits in LDS, shared
 // by the waves. The split's keys are cut into 32-key blocks dealt round-robin to the waves. Lane
 // (col, half) of a wave fetches half of the K row and half of the V row of key key0 + col: the K
-// half is directly its MFMA A fragment, the V half is transposed through a wave-private LDS tile.
+// half is directly its MFMA A fragment, the V half goes to a wave-private LDS tile that the PV
+// product reads back transposed.
 // The next block's fetch is issued before the current block's math (register double buffer).
 // A wave keeps an online softmax per column (no sink here), then the waves of the workgroup
 // merge through LDS in a fixed order:
@@ -35,8 +36,11 @@ template <typename E, int NCB>
 struct DecodeLds {
   static constexpr int kQStride = kDDQK + 16 / E::kBytes;  // Q^T rows (one per column), padded
   static constexpr int kQBytes = NCB * 32 * kQStride * E::kBytes;
-  static constexpr int kVStride = 32 + 4;  // V^T rows of one 32-key block
-  static constexpr int kVBytes = kDDV * kVStride * E::kBytes;
+  // one 32-key V block per wave: row-major [key][dv] for bf16 (read with the transposing LDS
+  // read), transposed [dv][key] for fp32; padded so operand reads hit distinct banks
+  static constexpr bool kVRowMajor = E::kBytes == 2;
+  static constexpr int kVStride = kVRowMajor ? kDDV + 16 : 32 + 4;
+  static constexpr int kVBytes = (kVRowMajor ? 32 : kDDV) * kVStride * E::kBytes;
   static constexpr int kMergeBytes = kDecNW * (kDDV / 32) * 16 * 64 * 4;  // one column block
   static constexpr int kWorkBytes = kDecNW * kVBytes > kMergeBytes ? kDecNW * kVBytes : kMergeBytes;
   static constexpr int kBytes = kQBytes + kWorkBytes + kDecNW * 64 * 4 * 2;
@@ -78,17 +82,15 @@ struct KeyRows {
     }
   }
 
-  // V^T[dv][key] <- this lane's V chunks (key = col); lanes of a half cover 32 consecutive keys.
-  __device__ __forceinline__ void store_vt(char* vt, int col, int half) const {
-    constexpr int S = DecodeLds<E, 1>::kVStride;
+  // This lane's V chunks (key = col, dv chunks 2i + half) -> the wave's V tile.
+  __device__ __forceinline__ void store_v(char* vt, int col, int half) const {
+    using L = DecodeLds<E, 1>;
+    constexpr int S = L::kVStride;
 #pragma unroll
     for (int i = 0; i < kVChunks; ++i) {
       const int dv0 = (2 * i + half) * E::kPerChunk;
-      if constexpr (E::kBytes == 2) {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(vt) + dv0 * S + col;
-#pragma unroll
-        for (int d = 0; d < 8; ++d)
-          dst[d * S] = (uint16_t)((d & 1) ? (v[i][d / 2] >> 16) : (v[i][d / 2] & 0xFFFFu));
+      if constexpr (L::kVRowMajor) {
+        st16(vt + (col * S + dv0) * E::kBytes, v[i]);
       } else {
         uint32_t* dst = reinterpret_cast<uint32_t*>(vt) + dv0 * S + col;
 #pragma unroll
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
   __syncthreads();  // Q^T is in LDS
 
   for (; key0 < s1; key0 += 32 * kDecNW) {
-    cur.store_vt(my_vt, col, half);
+    cur.store_v(my_vt, col, half);
     KeyRows<E> nxt;
     const int key_next = key0 + 32 * kDecNW;
     if (PREFETCH && key_next < s1) {
@@ -259,15 +261,11 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
         const Frag pf = frag_from_acc<E>(s[cb], 8 * ks);
 #pragma unroll
         for (int db = 0; db < kDDV / 32; ++db) {
-          const char* p = my_vt + ((32 * db + col) * Lds::kVStride + 16 * ks + 4 * half) * E::kBytes;
           Frag vf;
-          if constexpr (E::kBytes == 2) {
-            const u32x2 x = *reinterpret_cast<const u32x2*>(p);
-            const u32x2 y = *reinterpret_cast<const u32x2*>(p + 16);
-            u32x4 u;
-            u[0] = x[0]; u[1] = x[1]; u[2] = y[0]; u[3] = y[1];
-            vf = __builtin_bit_cast(bf16x8, u);
+          if constexpr (Lds::kVRowMajor) {
+            vf = vt_frag_tr(my_vt, Lds::kVStride, db, ks, lane);
           } else {
+            const char* p = my_vt + ((32 * db + col) * Lds::kVStride + 16 * ks + 4 * half) * E::kBytes;
             const f32x4 x = *reinterpret_cast<const f32x4*>(p);
             const f32x4 y = *reinterpret_cast<const f32x4*>(p + 32);
             vf[0] = x[0]; vf[1] = x[1]; vf[2] = x[2]; vf[3] = x[3];

@@ -23,7 +23,8 @@
 //   the next tile's diagonal block is loaded per step (prefetched under the current tile's math).
 //   The whole window is scored before the softmax, so it is single pass (no rescaling).
 // prefill_kernel (generic: global attention, fp32, other shapes): streams the union of the
-//   workgroup's windows in BK-key blocks, double-buffered in LDS, with an online softmax.
+//   workgroup's windows in BK-key blocks, double-buffered in LDS, with an online softmax whose
+//   running max is refreshed lazily (see below).
 #include "launch.hpp"
 
 namespace mimo {
@@ -32,49 +33,88 @@ constexpr int kDQK = 192;
 constexpr int kDV = 128;
 constexpr int kQT = 32;  // query positions per wave
 
+// LDS layout of one K/V block. K is row-major [key][dqk]. V is row-major [key][dv] for bf16 (read
+// back with the transposing LDS read) and transposed [dv][key] for fp32. Rows are padded so the
+// MFMA operand reads hit distinct banks.
 template <typename E, int BK>
 struct PrefillTile {
+  static constexpr bool kVRowMajor = E::kBytes == 2;
   static constexpr int kKStride = kDQK + 16 / E::kBytes;  // + 16 bytes: conflict-free b128 reads
-  static constexpr int kVStride = BK + 4;                 // V^T rows, + 4 elements
+  static constexpr int kVStride = kVRowMajor ? kDV + 16 : BK + 4;
   static constexpr int kKBytes = BK * kKStride * E::kBytes;
-  static constexpr int kVBytes = kDV * kVStride * E::kBytes;
+  static constexpr int kVBytes = (kVRowMajor ? BK : kDV) * kVStride * E::kBytes;
   static constexpr int kStageBytes = kKBytes + kVBytes;
   static_assert(kKBytes % 16 == 0 && kStageBytes % 16 == 0, "16-byte aligned stages");
 };
 
-// Global -> register -> LDS staging of one K block (row-major) and one V block (transposed).
-// K: consecutive threads take consecutive 16-byte chunks of a row (coalesced loads and stores).
-// V: thread chunk c holds key c % BK and dv chunk c / BK, so the lanes of a wave cover 32 or 64
-// consecutive keys of one dv range and their 2- or 4-byte transposed LDS writes hit distinct banks.
-// Keys at or past L are read from row L - 1 (finite data that the mask gives weight 0).
+// Global -> register -> LDS staging of one K block and one V block. Each thread moves a run of
+// consecutive 16-byte chunks of one row (KPT of K, VPT of V), so it needs a single offset per
+// tensor. For fp32 the V block is stored transposed ([dv][key]); there the chunks of thread t are
+// t + i * NT with key = chunk % BK, so a wave's lanes cover consecutive keys of one dv range and
+// its 4-byte transposed writes hit distinct banks.
+// Rows at or past L are read from row L - 1 (finite data that the mask gives weight 0).
 template <typename E, int NT, int BK>
 struct KVStager {
   using Tile = PrefillTile<E, BK>;
   static constexpr int kKChunksRow = kDQK / E::kPerChunk;
-  static constexpr int kKChunks = BK * kKChunksRow;
-  static constexpr int kKIt = (kKChunks + NT - 1) / NT;
-  static constexpr int kVChunks = BK * (kDV / E::kPerChunk);
-  static constexpr int kVIt = (kVChunks + NT - 1) / NT;
+  static constexpr int KPT = (BK * kKChunksRow + NT - 1) / NT;  // K chunks per thread
+  static_assert(kKChunksRow % KPT == 0, "a thread's K chunks stay in one row");
+  static constexpr int kKTpr = kKChunksRow / KPT;  // threads per K row
+  static constexpr int kKActive = BK * kKTpr;
+  static_assert(kKActive <= NT, "one pass covers the K block");
+  static constexpr int kVChunksRow = kDV / E::kPerChunk;
+  static constexpr int VPT = (BK * kVChunksRow + NT - 1) / NT;  // V chunks per thread
+  static_assert(!Tile::kVRowMajor || kVChunksRow % VPT == 0, "a thread's V chunks stay in one row");
+  static constexpr int kVTpr = kVChunksRow / VPT;
+  static constexpr int kVActive = Tile::kVRowMajor ? BK * kVTpr : NT;
 
-  u32x4 kr[kKIt];
-  u32x4 vr[kVIt];
+  u32x4 kr[KPT];
+  u32x4 vr[VPT];
+  uint32_t koff, voff[Tile::kVRowMajor ? 1 : VPT];
+  int krow, vrow;
 
-  __device__ __forceinline__ void load(const char* kbase, const char* vbase, size_t kstride,
-                                       size_t vstride, int key0, int L, int tid) {
+  __device__ __forceinline__ void init(size_t kstride, size_t vstride, int tid) {
+    krow = min(tid / kKTpr, BK - 1);
+    koff = (uint32_t)(krow * kstride + (tid % kKTpr) * KPT * 16);
+    if constexpr (Tile::kVRowMajor) {
+      vrow = min(tid / kVTpr, BK - 1);
+      voff[0] = (uint32_t)(vrow * vstride + (tid % kVTpr) * VPT * 16);
+    } else {
+      vrow = 0;
 #pragma unroll
-    for (int i = 0; i < kKIt; ++i) {
-      const int c = tid + i * NT;
-      if (kKChunks % NT == 0 || c < kKChunks) {
-        const int key = min(key0 + c / kKChunksRow, L - 1);
-        kr[i] = ld16(kbase + (size_t)key * kstride + (c % kKChunksRow) * 16);
+      for (int i = 0; i < VPT; ++i) {
+        const int c = tid + i * NT;
+        voff[i] = (uint32_t)((c % BK) * vstride + (c / BK) * 16);
       }
     }
+  }
+
+  // Loads the block starting at key0; only a block that reaches past L clamps its rows.
+  __device__ __forceinline__ void load(const char* kbase, const char* vbase, size_t kstride,
+                                       size_t vstride, int key0, int L, int tid) {
+    const bool tail = key0 + BK > L;
+    if (tid < kKActive) {
+      const char* p = kbase + (size_t)key0 * kstride + koff;
+      if (tail) p += ((size_t)min(key0 + krow, L - 1) - (key0 + krow)) * kstride;
 #pragma unroll
-    for (int i = 0; i < kVIt; ++i) {
-      const int c = tid + i * NT;
-      if (kVChunks % NT == 0 || c < kVChunks) {
-        const int key = min(key0 + c % BK, L - 1);
-        vr[i] = ld16(vbase + (size_t)key * vstride + (c / BK) * 16);
+      for (int i = 0; i < KPT; ++i) kr[i] = ld16(p + 16 * i);
+    }
+    if constexpr (Tile::kVRowMajor) {
+      if (tid < kVActive) {
+        const char* p = vbase + (size_t)key0 * vstride + voff[0];
+        if (tail) p += ((size_t)min(key0 + vrow, L - 1) - (key0 + vrow)) * vstride;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) vr[i] = ld16(p + 16 * i);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int c = tid + i * NT;
+        if (c >= BK * kVChunksRow) continue;
+        const int key = key0 + c % BK;
+        const char* p = vbase + (size_t)key0 * vstride + voff[i];
+        if (tail) p += ((size_t)min(key, L - 1) - key) * vstride;
+        vr[i] = ld16(p);
       }
     }
   }
@@ -82,25 +122,23 @@ struct KVStager {
   __device__ __forceinline__ void store(char* stage, int tid) const {
     char* sk = stage;
     char* sv = stage + Tile::kKBytes;
+    if (tid < kKActive) {
+      char* d = sk + (krow * Tile::kKStride) * E::kBytes + (tid % kKTpr) * KPT * 16;
 #pragma unroll
-    for (int i = 0; i < kKIt; ++i) {
-      const int c = tid + i * NT;
-      if (kKChunks % NT == 0 || c < kKChunks)
-        st16(sk + ((c / kKChunksRow) * Tile::kKStride) * E::kBytes + (c % kKChunksRow) * 16, kr[i]);
+      for (int i = 0; i < KPT; ++i) st16(d + 16 * i, kr[i]);
     }
+    if constexpr (Tile::kVRowMajor) {
+      if (tid < kVActive) {
+        char* d = sv + (vrow * Tile::kVStride) * E::kBytes + (tid % kVTpr) * VPT * 16;
 #pragma unroll
-    for (int i = 0; i < kVIt; ++i) {
-      const int c = tid + i * NT;
-      if (!(kVChunks % NT == 0 || c < kVChunks)) continue;
-      const int key = c % BK;
-      const int dv0 = (c / BK) * E::kPerChunk;
-      if constexpr (E::kBytes == 2) {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(sv) + dv0 * Tile::kVStride + key;
+        for (int i = 0; i < VPT; ++i) st16(d + 16 * i, vr[i]);
+      }
+    } else {
 #pragma unroll
-        for (int d = 0; d < 8; ++d)
-          dst[d * Tile::kVStride] = (uint16_t)((d & 1) ? (vr[i][d / 2] >> 16) : (vr[i][d / 2] & 0xFFFFu));
-      } else {
-        uint32_t* dst = reinterpret_cast<uint32_t*>(sv) + dv0 * Tile::kVStride + key;
+      for (int i = 0; i < VPT; ++i) {
+        const int c = tid + i * NT;
+        if (c >= BK * kVChunksRow) continue;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(sv) + (c / BK) * 4 * Tile::kVStride + c % BK;
 #pragma unroll
         for (int d = 0; d < 4; ++d) dst[d * Tile::kVStride] = vr[i][d];
       }
@@ -124,18 +162,17 @@ __device__ __forceinline__ typename E::Frag lds_k_frag(const char* sk, int row, 
   }
 }
 
-// A-operand fragment of V^T: dv row `row`; elements 0..3 are keys 16ks+4h..+3, 4..7 are keys
-// 16ks+8+4h..+3 (the key order in which the S^T accumulator holds P for this lane half).
+// A-operand fragment of V^T: dv row 32 db + lane % 32; elements 0..3 are keys 16ks+4h..+3,
+// 4..7 are keys 16ks+8+4h..+3 (the key order in which the S^T accumulator holds P for this lane
+// half).
 template <typename E, int BK>
-__device__ __forceinline__ typename E::Frag lds_vt_frag(const char* sv, int row, int ks, int half) {
-  const char* p = sv + (row * PrefillTile<E, BK>::kVStride + 16 * ks + 4 * half) * E::kBytes;
-  if constexpr (E::kBytes == 2) {
-    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
-    const u32x2 b = *reinterpret_cast<const u32x2*>(p + 16);
-    u32x4 u;
-    u[0] = a[0]; u[1] = a[1]; u[2] = b[0]; u[3] = b[1];
-    return __builtin_bit_cast(bf16x8, u);
+__device__ __forceinline__ typename E::Frag lds_vt_frag(const char* sv, int db, int ks, int lane) {
+  using Tile = PrefillTile<E, BK>;
+  if constexpr (Tile::kVRowMajor) {
+    return vt_frag_tr(sv, Tile::kVStride, db, ks, lane);
   } else {
+    const int half = lane >> 5, row = 32 * db + (lane & 31);
+    const char* p = sv + (row * Tile::kVStride + 16 * ks + 4 * half) * E::kBytes;
     const f32x4 a = *reinterpret_cast<const f32x4*>(p);
     const f32x4 b = *reinterpret_cast<const f32x4*>(p + 32);
     f32x8 f;
@@ -186,6 +223,11 @@ __device__ __forceinline__ void store_out_row(char* orow, const f32x16 (&acc)[kD
 }
 
 // ------------------------------------------------------------------------ generic streaming kernel
+
+constexpr float kLazyRescale = 8.f;  // log2 units
+#ifndef MIMO_SETPRIO
+#define MIMO_SETPRIO 0
+#endif
 
 template <typename E, int NW, int BK>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
@@ -244,6 +286,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   const int nblk = (P1 - kstart + BK - 1) / BK;
 
   KVStager<E, NT, BK> st;
+  st.init(krow_stride, vrow_stride, tid);
   st.load(kbase, vbase, krow_stride, vrow_stride, kstart, a.L, tid);
   st.store(smem, tid);
   wait_all();
@@ -262,11 +305,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
       f32x16 s[NSB];
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) s[sb] = zero16();
+      if (MIMO_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < kDQK / 16; ++kk)
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb)
           s[sb] = mma(lds_k_frag<E, BK>(sk, 32 * sb + col, kk, half), qf[kk], s[sb]);
+      if (MIMO_SETPRIO) __builtin_amdgcn_s_setprio(0);
 
       float bmax = -INFINITY;
 #pragma unroll
@@ -281,10 +326,21 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
           bmax = fmaxf(bmax, s[sb][r]);
         }
       }
-      bmax = halves_max(bmax) * c;
-      const float m_new = fmaxf(m, bmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
+      // lazy max: rescale only when some lane's block max exceeds its running max by more than
+      // kLazyRescale; otherwise exponentiate against the stale max (values stay below
+      // 2^kLazyRescale, and the same max scales l and acc, so the result is unchanged)
+      const float mb = halves_max(bmax) * c;
+      if (__builtin_amdgcn_ballot_w64(mb > m + kLazyRescale || (m == -INFINITY && mb > m)) != 0) {
+        const float m_new = fmaxf(m, mb);
+        const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.f : m_new));
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < kDV / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        m = m_new;
+      }
+      const float m_use = (m == -INFINITY) ? 0.f : m;
       float rs = 0.f;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
@@ -295,23 +351,17 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
           rs += p;
         }
       }
-      rs = halves_sum(rs);
-      l = l * alpha + rs;
-      m = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < kDV / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      }
+      l += halves_sum(rs);
 
+      if (MIMO_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
         const Frag pf = frag_from_acc<E>(s[ks >> 1], 8 * (ks & 1));
 #pragma unroll
         for (int db = 0; db < kDV / 32; ++db)
-          acc[db] = mma(lds_vt_frag<E, BK>(sv, 32 * db + col, ks, half), pf, acc[db]);
+          acc[db] = mma(lds_vt_frag<E, BK>(sv, db, ks, lane), pf, acc[db]);
       }
+      if (MIMO_SETPRIO) __builtin_amdgcn_s_setprio(0);
     }
 
     if (ib + 1 < nblk) st.store(smem + ((ib + 1) & 1) * Tile::kStageBytes, tid);
@@ -379,6 +429,8 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   {
     KVStager<E, NT, 32> pro[NB];
 #pragma unroll
+    for (int j = 0; j < NB; ++j) pro[j].init(krow_stride, vrow_stride, tid);
+#pragma unroll
     for (int j = 0; j < NB; ++j)
       if (t0 - NB + 1 + j >= 0)
         pro[j].load(kbase, vbase, krow_stride, vrow_stride, 32 * (t0 - NB + 1 + j), a.L, tid);
@@ -396,6 +448,7 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   __syncthreads();
 
   KVStager<E, NT, 32> st;
+  st.init(krow_stride, vrow_stride, tid);
   for (int t = t0; t < t1; ++t) {
     const int p0 = kQT * t;
     const int qpos = p0 + col;
@@ -466,8 +519,8 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < kDV / 32; ++db)
-          acc[db] = mma(lds_vt_frag<E, 32>(smem + base[j] + Tile::kKBytes, 32 * db + col, ks, half),
-                        pf[j][ks], acc[db]);
+          acc[db] = mma(lds_vt_frag<E, 32>(smem + base[j] + Tile::kKBytes, db, ks, lane), pf[j][ks],
+                        acc[db]);
 
     // ring update first, output stores last: the stores drain under the barrier and the next
     // tile's score MFMAs instead of holding up the loads that reuse their registers
