@@ -108,7 +108,9 @@ DecodePlan plan_decode(int B, int T, int Hq, int Hkv, int max_len, int window, i
   DecodePlan p{};
   const long long wmax = (long long)max_len + T;
   p.window = window < wmax ? window : (int)wmax;
-  const long long list_max = (long long)(max_len < p.window - 1 ? max_len : p.window - 1) + T;
+  // committed keys only: the new tokens are folded in by the last split
+  long long list_max = (long long)(max_len < p.window - 1 ? max_len : p.window - 1);
+  if (list_max < 1) list_max = 1;
   const long long blocks = (list_max + 31) / 32;
   long long ns;
   if (num_splits > 0) {

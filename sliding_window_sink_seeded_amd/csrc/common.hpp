@@ -59,6 +59,14 @@ __device__ __forceinline__ f32x16 mma(const f32x8& a, const f32x8& b, f32x16 acc
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Reinterprets 32 bits as a bf16 pair. Taken by value: with this toolchain,
+// __builtin_bit_cast(bf16x2, v[j]) on an ext-vector element silently reads element 0.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) {
+  bf16x2 r;
+  __builtin_memcpy(&r, &u, 4);
+  return r;
+}
+
 // fp32 pair -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v;

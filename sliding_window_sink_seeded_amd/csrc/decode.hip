@@ -6,9 +6,12 @@
 // cache does not grow with history) and > lightweight MTP > inference (the main model verifies the
 // drafted tokens in parallel, so one step carries 1 + drafts queries per sequence).
 //
-// Keys of sequence b form one logical list: committed positions [max(0, P - W + 1), P) read from
-// slot (p + off) mod C, then the T new tokens at positions P .. P+T-1. New token t sees positions
-// in [P + t - W + 1, P + t].
+// Keys of sequence b: committed positions [max(0, P - W + 1), P) read from slot (p + off) mod C,
+// and the T new tokens at positions P .. P+T-1. New token t sees positions in [P + t - W + 1,
+// P + t]. The committed keys are processed in 32-key MFMA blocks; the new tokens (at most 4) are
+// folded in afterwards by the last split, new token w by wave w, as one extra key per column
+// computed on the VALU (bf16 dot2). For a 128-key window this keeps the committed keys at exactly
+// four blocks, one per wave, instead of a fifth, nearly empty block on one wave.
 //
 // Work decomposition: one workgroup per (split, KV head g, sequence b). The G*T query columns of
 // (b, g) - every query head of the group times every new token - are the MFMA columns (32 per
@@ -24,6 +27,7 @@
 //   * several splits: the merged, unnormalised (m, l, acc) go to the workspace and
 //     combine_kernel folds the splits and the sink (counted once) into O / LSE.
 // Keys past the end of the split are fetched from its last key (finite data, masked to weight 0).
+// The running max is refreshed lazily (see update_max).
 #include "launch.hpp"
 
 namespace mimo {
@@ -41,9 +45,12 @@ struct DecodeLds {
   static constexpr bool kVRowMajor = E::kBytes == 2;
   static constexpr int kVStride = kVRowMajor ? kDDV + 16 : 32 + 4;
   static constexpr int kVBytes = (kVRowMajor ? 32 : kDDV) * kVStride * E::kBytes;
-  static constexpr int kMergeBytes = kDecNW * (kDDV / 32) * 16 * 64 * 4;  // one column block
+  static constexpr int kMergeBytes = kDecNW * 2 * 16 * 64 * 4;  // two dv blocks of one column block
   static constexpr int kWorkBytes = kDecNW * kVBytes > kMergeBytes ? kDecNW * kVBytes : kMergeBytes;
-  static constexpr int kBytes = kQBytes + kWorkBytes + kDecNW * 64 * 4 * 2;
+  // new-token K and V rows (T <= 4), staged with Q at kernel start
+  static constexpr int kNewKBytes = 4 * kDDQK * E::kBytes;
+  static constexpr int kNewBytes = kNewKBytes + 4 * kDDV * E::kBytes;
+  static constexpr int kBytes = kQBytes + kNewBytes + kWorkBytes + kDecNW * 64 * 4 * 2;
 };
 
 // One lane's share of a 32-key block: half of the K row (its MFMA A fragments) and half of the V
@@ -119,21 +126,19 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
   int P = a.cache_len[b];
   P = P < 0 ? 0 : (P > a.max_len ? a.max_len : P);
   const int off = a.cache_offset ? a.cache_offset[b] : 0;
+  // committed keys [list0, P) are split into ranges of keys_per_split (a multiple of 32); the
+  // T new tokens are folded in by the last split, one token per wave, on the VALU
   const int list0 = max(0, P - a.window + 1);
-  const int list1 = P + a.T;
   const int s0 = list0 + split * a.keys_per_split;
-  const int s1 = min(list1, s0 + a.keys_per_split);
+  const int s1 = min(P, s0 + a.keys_per_split);
 
   const size_t krow_bytes = (size_t)kDDQK * E::kBytes;
   const size_t vrow_bytes = (size_t)kDDV * E::kBytes;
   const char* kc = (const char*)a.k_cache + (size_t)g * krow_bytes;
   const char* vc = (const char*)a.v_cache + (size_t)g * vrow_bytes;
-  const char* kn = (const char*)a.k_new + (size_t)g * krow_bytes;
-  const char* vn = (const char*)a.v_new + (size_t)g * vrow_bytes;
   const size_t kstride = (size_t)a.Hkv * krow_bytes;  // between positions
   const size_t vstride = (size_t)a.Hkv * vrow_bytes;
   const size_t cache_row0 = (size_t)b * a.C;
-  const size_t new_row0 = (size_t)b * a.T;
 
   // Q^T of every query column (head j of the group x new token t, column c = j * T + t) -> LDS.
   char* sq = smem;
@@ -147,6 +152,20 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
         x = ld16((const char*)a.q + (((size_t)b * a.T + c % a.T) * a.Hq + head) * krow_bytes + ch * 16);
       }
       st16(sq + c * Lds::kQStride * E::kBytes + ch * 16, x);
+    }
+    // new-token K/V rows of this (b, g), read by the last split
+    if (split == a.nsplit - 1) {
+      constexpr int kKCh = kDDQK / E::kPerChunk, kVCh = kDDV / E::kPerChunk;
+      char* snew = smem + Lds::kQBytes;
+      for (int u = tid; u < a.T * (kKCh + kVCh); u += kDecNW * 64) {
+        const int t = u / (kKCh + kVCh), ch = u % (kKCh + kVCh);
+        if (ch < kKCh)
+          st16(snew + t * kDDQK * E::kBytes + ch * 16,
+               ld16((const char*)a.k_new + (((size_t)b * a.T + t) * a.Hkv + g) * krow_bytes + ch * 16));
+        else
+          st16(snew + Lds::kNewKBytes + t * kDDV * E::kBytes + (ch - kKCh) * 16,
+               ld16((const char*)a.v_new + (((size_t)b * a.T + t) * a.Hkv + g) * vrow_bytes + (ch - kKCh) * 16));
+      }
     }
   }
   int qpos[NCB];
@@ -165,18 +184,29 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
   // K and V row addresses of this lane's key in the block starting at key0 (clamped into the split)
   auto rows = [&](int key0, const char*& krow, const char*& vrow) {
     const int pos = min(key0 + col, s1 - 1);
-    if (pos < P) {
-      int slot = (pos + off) % a.C;
-      slot += slot < 0 ? a.C : 0;
-      krow = kc + (cache_row0 + slot) * kstride;
-      vrow = vc + (cache_row0 + slot) * vstride;
-    } else {
-      krow = kn + (new_row0 + (pos - P)) * kstride;
-      vrow = vn + (new_row0 + (pos - P)) * vstride;
+    int slot = (pos + off) % a.C;
+    slot += slot < 0 ? a.C : 0;
+    krow = kc + (cache_row0 + slot) * kstride;
+    vrow = vc + (cache_row0 + slot) * vstride;
+  };
+
+  // Lazy running max (log2 units): rescale l and acc only when some lane's candidate max exceeds
+  // its running max by more than 8; otherwise exponentiate against the stale max (exact: the same
+  // max scales l and acc).
+  auto update_max = [&](int cb, float mb) {
+    if (__builtin_amdgcn_ballot_w64(mb > m[cb] + 8.f || (m[cb] == -INFINITY && mb > m[cb])) != 0) {
+      const float m_new = fmaxf(m[cb], mb);
+      const float alpha = fast_exp2(m[cb] - (m_new == -INFINITY ? 0.f : m_new));
+      l[cb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDDV / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[cb][db][r] *= alpha;
+      m[cb] = m_new;
     }
   };
 
-  char* work = smem + Lds::kQBytes;
+  char* work = smem + Lds::kQBytes + Lds::kNewBytes;
   char* my_vt = work + wave * Lds::kVBytes;
   KeyRows<E> cur;
   int key0 = s0 + 32 * wave;
@@ -232,14 +262,11 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int pos = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int d = qpos[cb] - pos;
-        s[cb][r] = (d >= 0 && d < a.window && pos < s1) ? s[cb][r] : -INFINITY;
+        s[cb][r] = (qpos[cb] - pos < a.window && pos < s1) ? s[cb][r] : -INFINITY;
         bmax = fmaxf(bmax, s[cb][r]);
       }
-      bmax = halves_max(bmax) * c;
-      const float m_new = fmaxf(m[cb], bmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m[cb] - m_use);
+      update_max(cb, halves_max(bmax) * c);
+      const float m_use = (m[cb] == -INFINITY) ? 0.f : m[cb];
       float rs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -247,15 +274,7 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
         s[cb][r] = p;
         rs += p;
       }
-      rs = halves_sum(rs);
-      l[cb] = l[cb] * alpha + rs;
-      m[cb] = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < kDDV / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[cb][db][r] *= alpha;
-      }
+      l[cb] += halves_sum(rs);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const Frag pf = frag_from_acc<E>(s[cb], 8 * ks);
@@ -289,14 +308,72 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
     }
   }
 
-  // ---- merge the waves of this workgroup, one column block at a time (fixed order) ----
-  float* sm_acc = reinterpret_cast<float*>(work);  // [wave][db][r][lane]
+  // ---- new token `wave` (last split only): one extra key per column, on the VALU ----
+  if (split == a.nsplit - 1 && wave < a.T) {
+    const char* krow = smem + Lds::kQBytes + wave * kDDQK * E::kBytes;  // staged in LDS
+    const char* vrow = smem + Lds::kQBytes + Lds::kNewKBytes + wave * kDDV * E::kBytes;
+    const float c = a.scale_log2;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      // q . k over this lane half's 96 elements, then across halves
+      const char* qrow = sq + (cb * 32 + col) * Lds::kQStride * E::kBytes;
+      float dot = 0.f;
+      constexpr int kHalf = kDDQK / 2;
+#pragma unroll
+      for (int i = 0; i < kHalf / E::kPerChunk; ++i) {
+        const int e0 = kHalf * half + E::kPerChunk * i;
+        const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + e0 * E::kBytes);
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + e0 * E::kBytes);
+        if constexpr (E::kBytes == 2) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            dot = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[j]), as_bf16x2(kv[j]), dot, false);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dot = __builtin_fmaf(__uint_as_float(qv[j]), __uint_as_float(kv[j]), dot);
+        }
+      }
+      dot = halves_sum(dot);
+      const int ccol = cb * 32 + col;
+      const int t = ccol % a.T;
+      const bool vis = ccol < a.ncols && t >= wave && t - wave < a.window;
+      const float sc = vis ? dot * c : -INFINITY;
+      update_max(cb, sc);
+      const float p = fast_exp2(sc - ((m[cb] == -INFINITY) ? 0.f : m[cb]));
+      l[cb] += p;
+#pragma unroll
+      for (int db = 0; db < kDDV / 32; ++db) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int dv = 32 * db + 8 * gq + 4 * half;
+          float v[4];
+          if constexpr (E::kBytes == 2) {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(vrow + dv * 2);
+            v[0] = __uint_as_float(w[0] << 16);
+            v[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+            v[2] = __uint_as_float(w[1] << 16);
+            v[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+          } else {
+            const f32x4 w = *reinterpret_cast<const f32x4*>(vrow + dv * 4);
+            v[0] = w[0]; v[1] = w[1]; v[2] = w[2]; v[3] = w[3];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[cb][db][4 * gq + i] = __builtin_fmaf(p, v[i], acc[cb][db][4 * gq + i]);
+        }
+      }
+    }
+  }
+
+  // ---- merge the waves of this workgroup (fixed order): per column block, in two rounds of two
+  // dv blocks each; in round rr wave w sums dv block 2 rr + (w & 1), registers 8 (w >> 1) .. +7 ----
+  float* sm_acc = reinterpret_cast<float*>(work);  // [wave][2][r][lane]
   float* sm_m = reinterpret_cast<float*>(smem + (Lds::kBytes - kDecNW * 64 * 4 * 2));
   float* sm_l = sm_m + kDecNW * 64;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     __syncthreads();  // previous users of the work area are done
     sm_m[wave * 64 + lane] = m[cb];
+    sm_l[wave * 64 + lane] = l[cb];
     __syncthreads();
     const int c = cb * 32 + col;
     const bool cvalid = c < a.ncols;
@@ -309,60 +386,65 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
     const float s_l2 = fold_sink ? a.sink[head] * kLog2e : -INFINITY;
     M = fmaxf(M, s_l2);
     const float M_use = (M == -INFINITY) ? 0.f : M;
-    const float scale_w = fast_exp2(m[cb] - M_use);
-#pragma unroll
-    for (int db = 0; db < kDDV / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sm_acc[((wave * (kDDV / 32) + db) * 16 + r) * 64 + lane] = acc[cb][db][r] * scale_w;
-    sm_l[wave * 64 + lane] = l[cb] * scale_w;
-    __syncthreads();
     float Lsum = fold_sink ? fast_exp2(s_l2 - M_use) : 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecNW; ++w) Lsum += sm_l[w * 64 + lane];
-    // wave w reduces dv block db = w (kDecNW == kDDV / 32)
-    const int db = wave;
-    f32x16 o = zero16();
+    for (int w = 0; w < kDecNW; ++w) Lsum += sm_l[w * 64 + lane] * fast_exp2(sm_m[w * 64 + lane] - M_use);
+    const float scale_w = fast_exp2(m[cb] - M_use);
 #pragma unroll
-    for (int w = 0; w < kDecNW; ++w)
+    for (int rr = 0; rr < 2; ++rr) {
+      if (rr) __syncthreads();  // round 0 reads are done
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[r] += sm_acc[((w * (kDDV / 32) + db) * 16 + r) * 64 + lane];
-    if (cvalid && a.nsplit == 1) {
-      const float inv = 1.f / Lsum;
-      char* orow = (char*)a.o + (((size_t)b * a.T + t) * a.Hq + head) * kDDV * E::kBytes;
+      for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int dv = 32 * db + 8 * gq + 4 * half;
-        const float x0 = o[4 * gq] * inv, x1 = o[4 * gq + 1] * inv;
-        const float x2 = o[4 * gq + 2] * inv, x3 = o[4 * gq + 3] * inv;
-        if constexpr (E::kBytes == 2) {
-          u32x2 w;
-          w[0] = pack_bf16x2(x0, x1);
-          w[1] = pack_bf16x2(x2, x3);
-          *reinterpret_cast<u32x2*>(orow + dv * 2) = w;
-        } else {
-          f32x4 w;
-          w[0] = x0; w[1] = x1; w[2] = x2; w[3] = x3;
-          *reinterpret_cast<f32x4*>(orow + dv * 4) = w;
+        for (int r = 0; r < 16; ++r)
+          sm_acc[((wave * 2 + d2) * 16 + r) * 64 + lane] = acc[cb][2 * rr + d2][r] * scale_w;
+      __syncthreads();
+      const int db = 2 * rr + (wave & 1), rb = 8 * (wave >> 1);
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        o[i] = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDecNW; ++w) o[i] += sm_acc[((w * 2 + (wave & 1)) * 16 + rb + i) * 64 + lane];
+      }
+      if (!cvalid) continue;
+      if (a.nsplit == 1) {
+        const float inv = 1.f / Lsum;
+        char* orow = (char*)a.o + (((size_t)b * a.T + t) * a.Hq + head) * kDDV * E::kBytes;
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int dv = 32 * db + 8 * ((rb >> 2) + g2) + 4 * half;
+          const float x0 = o[4 * g2] * inv, x1 = o[4 * g2 + 1] * inv;
+          const float x2 = o[4 * g2 + 2] * inv, x3 = o[4 * g2 + 3] * inv;
+          if constexpr (E::kBytes == 2) {
+            u32x2 w;
+            w[0] = pack_bf16x2(x0, x1);
+            w[1] = pack_bf16x2(x2, x3);
+            *reinterpret_cast<u32x2*>(orow + dv * 2) = w;
+          } else {
+            f32x4 w;
+            w[0] = x0; w[1] = x1; w[2] = x2; w[3] = x3;
+            *reinterpret_cast<f32x4*>(orow + dv * 4) = w;
+          }
         }
-      }
-      if (a.lse && wave == 0 && half == 0)
-        a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(Lsum)) * kLn2;
-    } else if (cvalid) {
-      // partial record for (b, g, split, column c): acc[kDDV], m, l
-      const int ncols_pad = NCB * 32;
-      float* rec = a.ws + ((((size_t)b * a.Hkv + g) * a.nsplit + split) * ncols_pad + c) * (kDDV + 2);
+        if (a.lse && rr == 0 && wave == 0 && half == 0)
+          a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(Lsum)) * kLn2;
+      } else {
+        // partial record for (b, g, split, column c): acc[kDDV], m, l
+        const int ncols_pad = NCB * 32;
+        float* rec = a.ws + ((((size_t)b * a.Hkv + g) * a.nsplit + split) * ncols_pad + c) * (kDDV + 2);
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        float* dst = rec + 32 * db + 8 * gq + 4 * half;  // records are only 8-byte aligned
-        dst[0] = o[4 * gq];
-        dst[1] = o[4 * gq + 1];
-        dst[2] = o[4 * gq + 2];
-        dst[3] = o[4 * gq + 3];
-      }
-      if (wave == 0 && half == 0) {
-        rec[kDDV] = M;
-        rec[kDDV + 1] = Lsum;
+        for (int g2 = 0; g2 < 2; ++g2) {
+          float* dst = rec + 32 * db + 8 * ((rb >> 2) + g2) + 4 * half;  // records are 8-byte aligned
+          dst[0] = o[4 * g2];
+          dst[1] = o[4 * g2 + 1];
+          dst[2] = o[4 * g2 + 2];
+          dst[3] = o[4 * g2 + 3];
+        }
+        if (rr == 0 && wave == 0 && half == 0) {
+          rec[kDDV] = M;
+          rec[kDDV + 1] = Lsum;
+        }
       }
     }
   }
