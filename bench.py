@@ -31,6 +31,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA peaks, TFLOP/s
 MALL_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = os.path.join(ROOT, "sliding_window_sink_seeded_amd", "csrc")
 
 METRIC = "prefill attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
 
@@ -233,6 +235,40 @@ def cpu_baseline(case, target_s=12.0):
             "sample": sample, "seconds": round(t, 2)}
 
 
+def kernel_source_digest(kind):
+    """sha256 over the HIP sources (names and bytes) that build and launch the `kind` kernels."""
+    import hashlib
+
+    names = ["api.hip", "common.hpp", "launch.hpp", "prefill.hip" if kind == "prefill" else "decode.hip"]
+    h = hashlib.sha256()
+    for name in names:
+        h.update(name.encode())
+        with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kind):
+    """HBM bytes per launch of the workload's dominant kernel from its committed counter summary
+    (FETCH_SIZE / WRITE_SIZE, scaled by a plain copy's counters), or None when there is no summary
+    or the kernel sources have changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                fields[k.strip("`")] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_digest(kind):
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def describe(case, wall_ms, event_ms):
     w = case.w
     tflops = case.flops / (wall_ms * 1e-3) / 1e12
@@ -300,7 +336,7 @@ def main():
         bound, unit = "hbm", "GB/s"
         achieved, peak, per_launch = case.bytes / (event_ms * 1e-3) / 1e9, HBM_PEAK_GBS, case.bytes
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name, w.kind),
                 "algorithmic_per_launch": per_launch, "kernel_avg_ms": round(event_ms, 4)}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(case)
