@@ -31,6 +31,7 @@ int group_heads(int Hq, int Hkv, const int32_t* kv_head_of_q, mimo::HeadList* hl
   const int G = Hq / Hkv;
   if (!kv_head_of_q) {
     for (int h = 0; h < Hq; ++h) hl->heads[h] = (int16_t)h;
+    hl->identity = 1;
     return MIMO_OK;
   }
   int fill[mimo::kMaxHeads] = {0};
@@ -40,7 +41,10 @@ int group_heads(int Hq, int Hkv, const int32_t* kv_head_of_q, mimo::HeadList* hl
     if (fill[g] >= G) return fail(MIMO_EINVAL, "KV head %d serves more than Hq/Hkv = %d query heads", g, G);
     hl->heads[g * G + fill[g]++] = (int16_t)h;
   }
-  return MIMO_OK;  // every KV head now has exactly G heads (counts sum to Hq)
+  // every KV head now has exactly G heads (counts sum to Hq)
+  hl->identity = 1;
+  for (int h = 0; h < Hq; ++h) hl->identity &= hl->heads[h] == h;
+  return MIMO_OK;
 }
 
 int check_common(int dt, int B, int Hq, int Hkv, int d_qk, int d_v, int window, float scale) {

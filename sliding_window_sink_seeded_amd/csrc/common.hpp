@@ -202,9 +202,21 @@ __device__ __forceinline__ bf16x8 vt_frag_tr(const char* vtile, int row_elems, i
   return __builtin_bit_cast(bf16x8, u);
 }
 
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 // Query heads grouped by KV head: heads[g * G + j] is the j-th query head served by KV head g.
+// With the default map (identity set) that is g * G + j itself and the table is not read: a
+// per-lane table read is a memory load whose wait would also hold back every load issued before it.
 struct HeadList {
+  int identity;
   int16_t heads[kMaxHeads];
+  __device__ __forceinline__ int at(int i) const {
+    if (identity) return i;
+    return heads[i];
+  }
 };
 
 }  // namespace mimo

@@ -140,34 +140,83 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
   const size_t vstride = (size_t)a.Hkv * vrow_bytes;
   const size_t cache_row0 = (size_t)b * a.C;
 
-  // Q^T of every query column (head j of the group x new token t, column c = j * T + t) -> LDS.
+  // K and V row addresses of this lane's key in the block starting at key0 (clamped into the split)
+  auto rows = [&](int key0, const char*& krow, const char*& vrow) {
+    const int pos = min(key0 + col, s1 - 1);
+    int slot = (pos + off) % a.C;
+    slot += slot < 0 ? a.C : 0;
+    krow = kc + (cache_row0 + slot) * kstride;
+    vrow = vc + (cache_row0 + slot) * vstride;
+  };
+
+  KeyRows<E> cur;
+  int key0 = s0 + 32 * wave;
+
+  // Q^T of every query column (head j of the group x new token t, column c = j * T + t) -> LDS,
+  // and (last split) the new tokens' K/V rows of this (b, g). Every load of a thread is issued
+  // before its first LDS store, and the first K/V block's fetch goes out before those stores so
+  // that its latency overlaps them. A non-default head map is read before any other load, so
+  // that waiting for it waits for nothing else.
   char* sq = smem;
   {
     constexpr int kChunksRow = kDDQK / E::kPerChunk;
-    for (int u = tid; u < NCB * 32 * kChunksRow; u += kDecNW * 64) {
-      const int c = u / kChunksRow, ch = u % kChunksRow;
-      u32x4 x = zero_chunk();
-      if (c < a.ncols) {
-        const int head = a.hl.heads[g * a.G + c / a.T];
-        x = ld16((const char*)a.q + (((size_t)b * a.T + c % a.T) * a.Hq + head) * krow_bytes + ch * 16);
-      }
-      st16(sq + c * Lds::kQStride * E::kBytes + ch * 16, x);
+    constexpr int kQChunks = NCB * 32 * kChunksRow;
+    constexpr int kQPer = (kQChunks + kDecNW * 64 - 1) / (kDecNW * 64);
+    constexpr int kKCh = kDDQK / E::kPerChunk, kVCh = kDDV / E::kPerChunk;
+    constexpr int kNewPer = (4 * (kKCh + kVCh) + kDecNW * 64 - 1) / (kDecNW * 64);
+    int head[kQPer];
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) {
+      const int c = min((tid + i * kDecNW * 64) / kChunksRow, a.ncols - 1);  // padding: any valid row
+      head[i] = g * a.G + c / a.T;
     }
-    // new-token K/V rows of this (b, g), read by the last split
-    if (split == a.nsplit - 1) {
-      constexpr int kKCh = kDDQK / E::kPerChunk, kVCh = kDDV / E::kPerChunk;
-      char* snew = smem + Lds::kQBytes;
-      for (int u = tid; u < a.T * (kKCh + kVCh); u += kDecNW * 64) {
-        const int t = u / (kKCh + kVCh), ch = u % (kKCh + kVCh);
+    if (!a.hl.identity) {
+#pragma unroll
+      for (int i = 0; i < kQPer; ++i) head[i] = a.hl.heads[head[i]];
+    }
+    u32x4 xq[kQPer], xn[kNewPer];
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) {
+      const int u = tid + i * kDecNW * 64;
+      const int c = min(u / kChunksRow, a.ncols - 1), ch = u % kChunksRow;
+      xq[i] = ld16((const char*)a.q + (((size_t)b * a.T + c % a.T) * a.Hq + head[i]) * krow_bytes + ch * 16);
+    }
+    const bool last = split == a.nsplit - 1;
+#pragma unroll
+    for (int i = 0; i < kNewPer; ++i) {
+      const int u = tid + i * kDecNW * 64;
+      const int t = min(u / (kKCh + kVCh), a.T - 1), ch = u % (kKCh + kVCh);
+      const char* src = ch < kKCh
+                            ? (const char*)a.k_new + (((size_t)b * a.T + t) * a.Hkv + g) * krow_bytes + ch * 16
+                            : (const char*)a.v_new + (((size_t)b * a.T + t) * a.Hkv + g) * vrow_bytes +
+                                  (ch - kKCh) * 16;
+      xn[i] = ld16(src);
+    }
+    if (key0 < s1) {
+      const char *kr, *vr;
+      rows(key0, kr, vr);
+      cur.load(kr, vr, half);
+    }
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) {
+      const int u = tid + i * kDecNW * 64;
+      const int c = u / kChunksRow, ch = u % kChunksRow;
+      if (u < kQChunks) st16(sq + c * Lds::kQStride * E::kBytes + ch * 16, c < a.ncols ? xq[i] : zero_chunk());
+    }
+    char* snew = smem + Lds::kQBytes;
+#pragma unroll
+    for (int i = 0; i < kNewPer; ++i) {
+      const int u = tid + i * kDecNW * 64;
+      const int t = u / (kKCh + kVCh), ch = u % (kKCh + kVCh);
+      if (last && t < a.T) {
         if (ch < kKCh)
-          st16(snew + t * kDDQK * E::kBytes + ch * 16,
-               ld16((const char*)a.k_new + (((size_t)b * a.T + t) * a.Hkv + g) * krow_bytes + ch * 16));
+          st16(snew + t * kDDQK * E::kBytes + ch * 16, xn[i]);
         else
-          st16(snew + Lds::kNewKBytes + t * kDDV * E::kBytes + (ch - kKCh) * 16,
-               ld16((const char*)a.v_new + (((size_t)b * a.T + t) * a.Hkv + g) * vrow_bytes + (ch - kKCh) * 16));
+          st16(snew + Lds::kNewKBytes + t * kDDV * E::kBytes + (ch - kKCh) * 16, xn[i]);
       }
     }
   }
+
   int qpos[NCB];
   float m[NCB], l[NCB];
   f32x16 acc[NCB][kDDV / 32];
@@ -180,15 +229,6 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
 #pragma unroll
     for (int db = 0; db < kDDV / 32; ++db) acc[cb][db] = zero16();
   }
-
-  // K and V row addresses of this lane's key in the block starting at key0 (clamped into the split)
-  auto rows = [&](int key0, const char*& krow, const char*& vrow) {
-    const int pos = min(key0 + col, s1 - 1);
-    int slot = (pos + off) % a.C;
-    slot += slot < 0 ? a.C : 0;
-    krow = kc + (cache_row0 + slot) * kstride;
-    vrow = vc + (cache_row0 + slot) * vstride;
-  };
 
   // Lazy running max (log2 units): rescale l and acc only when some lane's candidate max exceeds
   // its running max by more than 8; otherwise exponentiate against the stale max (exact: the same
@@ -208,14 +248,7 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
 
   char* work = smem + Lds::kQBytes + Lds::kNewBytes;
   char* my_vt = work + wave * Lds::kVBytes;
-  KeyRows<E> cur;
-  int key0 = s0 + 32 * wave;
-  if (key0 < s1) {
-    const char *kr, *vr;
-    rows(key0, kr, vr);
-    cur.load(kr, vr, half);
-  }
-  __syncthreads();  // Q^T is in LDS
+  __syncthreads();  // Q^T and the new-token rows are in LDS
 
   for (; key0 < s1; key0 += 32 * kDecNW) {
     cur.store_v(my_vt, col, half);
@@ -378,7 +411,7 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
     const int c = cb * 32 + col;
     const bool cvalid = c < a.ncols;
     const int t = cvalid ? c % a.T : 0;
-    const int head = cvalid ? a.hl.heads[g * a.G + c / a.T] : 0;
+    const int head = cvalid ? a.hl.at(g * a.G + c / a.T) : 0;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kDecNW; ++w) M = fmaxf(M, sm_m[w * 64 + lane]);
@@ -460,7 +493,7 @@ __global__ __launch_bounds__(kDDV) void combine_kernel(const DecodeArgs a) {
   const int dv = threadIdx.x;
   const int ncols_pad = ((a.ncols + 31) / 32) * 32;
   const int t = c % a.T;
-  const int head = a.hl.heads[g * a.G + c / a.T];
+  const int head = a.hl.at(g * a.G + c / a.T);
   const float* base = a.ws + (((size_t)b * a.Hkv + g) * a.nsplit * ncols_pad + c) * (kDDV + 2);
   const size_t stride = (size_t)ncols_pad * (kDDV + 2);
 

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
 
   const int HG = a.heads_per_wg;
   const int qtiles = NW / HG;
-  const int head = a.hl.heads[g * a.G + hc * HG + wave % HG];
+  const int head = a.hl.at(g * a.G + hc * HG + wave % HG);
   const int P0 = qb * kQT * qtiles;
   const int P1 = min(a.L, P0 + kQT * qtiles);
   const int p0 = P0 + kQT * (wave / HG);  // this wave's first query position
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   rest /= a.n_hchunks;
   const int g = rest % a.Hkv;
   const int b = rest / a.Hkv;
-  const int head = a.hl.heads[g * a.G + hc * NW + wave];
+  const int head = a.hl.at(g * a.G + hc * NW + wave);
 
   const int n_tiles = (a.L + kQT - 1) / kQT;
   const int t0 = seg * a.tiles_per_wg;
