@@ -449,7 +449,9 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
 
   KVStager<E, NT, 32> st;
   st.init(krow_stride, vrow_stride, tid);
-  for (int t = t0; t < t1; ++t) {
+  // one tile; the next tile's Q goes to the second register set, fetched before this tile's score
+  // MFMAs (Q of tiles t0, t0 + 2, .. lives in qf, of t0 + 1, t0 + 3, .. in qg)
+  auto step = [&](const int t, bf16x8(&qc)[kDQK / 16], bf16x8(&qn)[kDQK / 16]) {
     const int p0 = kQT * t;
     const int qpos = p0 + col;
     const bool has_next = t + 1 < t1;
@@ -457,21 +459,23 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) base[j] = slot(t - NB + 1 + j) * Tile::kStageBytes;
 
+    // the next tile's diagonal K/V block and Q stream in under this whole tile. The loads are
+    // unconditional (on the last tile: this tile's block again, and one shared Q row, unused), so
+    // that the compiler's wait counts see one straight-line sequence of loads and stores.
+    st.load(kbase, vbase, krow_stride, vrow_stride, 32 * min(t + 1, t1 - 1), a.L, tid);
+    const char* qrow_next = has_next ? qbase + (size_t)min(qpos + kQT, a.L - 1) * qrow_stride : qbase;
+#pragma unroll
+    for (int kk = 0; kk < kDQK / 16; ++kk) qn[kk] = global_q_frag<E>(qrow_next, kk, half);
+    __builtin_amdgcn_sched_barrier(0);  // left alone, the scheduler sinks the Q loads below the MFMAs
+
     // scores of the whole window: block j holds keys 32 * (t - NB + 1 + j) ..
     f32x16 s[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) s[j] = zero16();
 #pragma unroll
-    for (int kk = 0; kk < kDQK / 16; ++kk)
+    for (int kk = 0; kk < kDQK / 16; ++kk) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) s[j] = mma(lds_k_frag<E, 32>(smem + base[j], col, kk, half), qf[kk], s[j]);
-
-    // the next tile's Q and diagonal K/V block stream in under this tile's softmax and P.V
-    if (has_next) {
-      const char* qrow = qbase + (size_t)min(qpos + kQT, a.L - 1) * qrow_stride;
-#pragma unroll
-      for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
-      st.load(kbase, vbase, krow_stride, vrow_stride, 32 * (t + 1), a.L, tid);
+      for (int j = 0; j < NB; ++j) s[j] = mma(lds_k_frag<E, 32>(smem + base[j], col, kk, half), qc[kk], s[j]);
     }
 
     float rmax = -INFINITY;
@@ -532,6 +536,11 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
       if (a.lse && half == 0) a.lse[((size_t)b * a.Hq + head) * a.L + qpos] = (m + fast_log2(l)) * kLn2;
     }
     __syncthreads();
+  };
+  bf16x8 qg[kDQK / 16];
+  for (int t = t0; t < t1; t += 2) {
+    step(t, qf, qg);
+    if (t + 1 < t1) step(t + 1, qg, qf);
   }
 }
 
