@@ -93,7 +93,7 @@ struct KVStager {
   __device__ __forceinline__ void load(const char* kbase, const char* vbase, size_t kstride,
                                        size_t vstride, int key0, int L, int tid) {
     const bool tail = key0 + BK > L;
-    if (tid < kKActive) {
+    {  // every thread loads (the spare ones re-read a chunk of the last row; only store() skips them)
       const char* p = kbase + (size_t)key0 * kstride + koff;
       if (tail) p += ((size_t)min(key0 + krow, L - 1) - (key0 + krow)) * kstride;
 #pragma unroll
@@ -453,7 +453,9 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   // MFMAs (Q of tiles t0, t0 + 2, .. lives in qf, of t0 + 1, t0 + 3, .. in qg)
   auto step = [&](const int t, bf16x8(&qc)[kDQK / 16], bf16x8(&qn)[kDQK / 16]) {
     const int p0 = kQT * t;
-    const int qpos = p0 + col;
+    // lanes past the end of the sequence stand in for its last row: same Q, same keys, same
+    // result, stored to the same place, so no store or load below needs a per-lane condition
+    const int qpos = min(p0 + col, a.L - 1);
     const bool has_next = t + 1 < t1;
     int base[NB];  // byte offset of each window block's ring slot
 #pragma unroll
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
     // unconditional (on the last tile: this tile's block again, and one shared Q row, unused), so
     // that the compiler's wait counts see one straight-line sequence of loads and stores.
     st.load(kbase, vbase, krow_stride, vrow_stride, 32 * min(t + 1, t1 - 1), a.L, tid);
-    const char* qrow_next = has_next ? qbase + (size_t)min(qpos + kQT, a.L - 1) * qrow_stride : qbase;
+    const char* qrow_next = has_next ? qbase + (size_t)min(p0 + kQT + col, a.L - 1) * qrow_stride : qbase;
 #pragma unroll
     for (int kk = 0; kk < kDQK / 16; ++kk) qn[kk] = global_q_frag<E>(qrow_next, kk, half);
     __builtin_amdgcn_sched_barrier(0);  // left alone, the scheduler sinks the Q loads below the MFMAs
@@ -531,10 +533,8 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
     u32x4 out[8];
     pack_row_bf16(acc, 1.f / l, out);
     if (has_next) st.store(smem + slot(t + 1) * Tile::kStageBytes, tid);
-    if (qpos < a.L) {
-      store_packed_row_bf16(obase + (size_t)qpos * orow_stride, out, half);
-      if (a.lse && half == 0) a.lse[((size_t)b * a.Hq + head) * a.L + qpos] = (m + fast_log2(l)) * kLn2;
-    }
+    store_packed_row_bf16(obase + (size_t)qpos * orow_stride, out, half);
+    if (a.lse) a.lse[((size_t)b * a.Hq + head) * a.L + qpos] = (m + fast_log2(l)) * kLn2;
     __syncthreads();
   };
   bf16x8 qg[kDQK / 16];
