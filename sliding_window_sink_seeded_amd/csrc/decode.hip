@@ -35,6 +35,8 @@ namespace mimo {
 constexpr int kDDQK = 192;
 constexpr int kDDV = 128;
 constexpr int kDecNW = 4;  // waves per workgroup
+// split partial record of one query column: acc[kDDV], m, l, two pad floats (16-byte rows)
+constexpr int kRec = kDDV + 4;
 
 template <typename E, int NCB>
 struct DecodeLds {
@@ -465,14 +467,12 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
       } else {
         // partial record for (b, g, split, column c): acc[kDDV], m, l
         const int ncols_pad = NCB * 32;
-        float* rec = a.ws + ((((size_t)b * a.Hkv + g) * a.nsplit + split) * ncols_pad + c) * (kDDV + 2);
+        float* rec = a.ws + ((((size_t)b * a.Hkv + g) * a.nsplit + split) * ncols_pad + c) * kRec;
 #pragma unroll
         for (int g2 = 0; g2 < 2; ++g2) {
-          float* dst = rec + 32 * db + 8 * ((rb >> 2) + g2) + 4 * half;  // records are 8-byte aligned
-          dst[0] = o[4 * g2];
-          dst[1] = o[4 * g2 + 1];
-          dst[2] = o[4 * g2 + 2];
-          dst[3] = o[4 * g2 + 3];
+          f32x4 w;
+          w[0] = o[4 * g2]; w[1] = o[4 * g2 + 1]; w[2] = o[4 * g2 + 2]; w[3] = o[4 * g2 + 3];
+          *reinterpret_cast<f32x4*>(rec + 32 * db + 8 * ((rb >> 2) + g2) + 4 * half) = w;
         }
         if (rr == 0 && wave == 0 && half == 0) {
           rec[kDDV] = M;
@@ -483,45 +483,77 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a)
   }
 }
 
-// One workgroup of kDDV threads per output row (b, t, head): fold the split partials and the
-// sink (once) into O and LSE.
+// Folds the split partials and the sink (once) into O and LSE. A workgroup covers kCombCols query
+// columns of one (b, g); thread (column, quad) owns 4 consecutive dv of that column. Pass 1 takes
+// the max over the splits' m, pass 2 sums the rescaled l and acc, kCombUnroll splits at a time so
+// that their loads are in flight together.
+constexpr int kCombCols = 8;
+constexpr int kCombUnroll = 8;
+
 template <typename E>
-__global__ __launch_bounds__(kDDV) void combine_kernel(const DecodeArgs a) {
-  const int c = blockIdx.x;  // query column within the group
+__global__ __launch_bounds__(kCombCols * kDDV / 4) void combine_kernel(const DecodeArgs a) {
+  const int quad = threadIdx.x % (kDDV / 4);
+  const int c = blockIdx.x * kCombCols + threadIdx.x / (kDDV / 4);  // query column within the group
   const int g = blockIdx.y;
   const int b = blockIdx.z;
-  const int dv = threadIdx.x;
+  if (c >= a.ncols) return;
   const int ncols_pad = ((a.ncols + 31) / 32) * 32;
   const int t = c % a.T;
   const int head = a.hl.at(g * a.G + c / a.T);
-  const float* base = a.ws + (((size_t)b * a.Hkv + g) * a.nsplit * ncols_pad + c) * (kDDV + 2);
-  const size_t stride = (size_t)ncols_pad * (kDDV + 2);
+  const float* base = a.ws + (((size_t)b * a.Hkv + g) * a.nsplit * ncols_pad + c) * kRec;
+  const size_t stride = (size_t)ncols_pad * kRec;
+  const int ns = a.nsplit;
 
-  float M = a.sink ? a.sink[head] * kLog2e : -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, base[s * stride + kDDV]);
-  const float M_use = (M == -INFINITY) ? 0.f : M;
-  float L = a.sink ? fast_exp2(a.sink[head] * kLog2e - M_use) : 0.f;
-  float o = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float* rec = base + s * stride;
-    const float w = fast_exp2(rec[kDDV] - M_use);  // empty split: m = -inf -> weight 0
-    L += rec[kDDV + 1] * w;
-    o += rec[dv] * w;
+  const float sink_l2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
+  float M = sink_l2;
+  for (int s0 = 0; s0 < ns; s0 += kCombUnroll) {
+    float mv[kCombUnroll];
+#pragma unroll
+    for (int u = 0; u < kCombUnroll; ++u) mv[u] = base[(size_t)min(s0 + u, ns - 1) * stride + kDDV];
+#pragma unroll
+    for (int u = 0; u < kCombUnroll; ++u) M = fmaxf(M, mv[u]);  // clamped repeats change no max
   }
-  o /= L;
+  const float M_use = (M == -INFINITY) ? 0.f : M;
+  float L = a.sink ? fast_exp2(sink_l2 - M_use) : 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < ns; s0 += kCombUnroll) {
+    f32x4 acc[kCombUnroll];
+    f32x2 ml[kCombUnroll];
+#pragma unroll
+    for (int u = 0; u < kCombUnroll; ++u) {
+      const float* rec = base + (size_t)min(s0 + u, ns - 1) * stride;
+      acc[u] = *reinterpret_cast<const f32x4*>(rec + 4 * quad);
+      ml[u] = *reinterpret_cast<const f32x2*>(rec + kDDV);
+    }
+#pragma unroll
+    for (int u = 0; u < kCombUnroll; ++u) {
+      // past the last split: weight 0; an empty split has m = -inf, also weight 0
+      const float w = s0 + u < ns ? fast_exp2(ml[u][0] - M_use) : 0.f;
+      L += ml[u][1] * w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] += acc[u][i] * w;
+    }
+  }
+  const float inv = 1.f / L;
   char* orow = (char*)a.o + (((size_t)b * a.T + t) * a.Hq + head) * kDDV * E::kBytes;
   if constexpr (E::kBytes == 2) {
-    reinterpret_cast<uint16_t*>(orow)[dv] = (uint16_t)bf16_bits(o);
+    u32x2 w;
+    w[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
+    w[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+    *reinterpret_cast<u32x2*>(orow + 8 * quad) = w;
   } else {
-    reinterpret_cast<float*>(orow)[dv] = o;
+    f32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = o[i] * inv;
+    *reinterpret_cast<f32x4*>(orow + 16 * quad) = w;
   }
-  if (a.lse && dv == 0) a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(L)) * kLn2;
+  if (a.lse && quad == 0) a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(L)) * kLn2;
 }
 
 size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit) {
   if (nsplit <= 1) return 0;
   const size_t ncols_pad = (size_t)((ncols + 31) / 32) * 32;
-  return (size_t)B * Hkv * nsplit * ncols_pad * (kDDV + 2) * sizeof(float);
+  return (size_t)B * Hkv * nsplit * ncols_pad * kRec * sizeof(float);
 }
 
 // With one column block (e.g. 8 query heads x 4 tokens) a wave holds few blocks and fewer
@@ -544,11 +576,12 @@ hipError_t decode_launch(bool bf16, const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_kernel<F32, 1, false>), grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  const dim3 cgrid(a.ncols, a.Hkv, a.B);
+  const dim3 cgrid((a.ncols + kCombCols - 1) / kCombCols, a.Hkv, a.B);
+  const dim3 cblock(kCombCols * kDDV / 4);
   if (bf16)
-    hipLaunchKernelGGL(combine_kernel<BF16>, cgrid, dim3(kDDV), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel<BF16>, cgrid, cblock, 0, stream, a);
   else
-    hipLaunchKernelGGL(combine_kernel<F32>, cgrid, dim3(kDDV), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel<F32>, cgrid, cblock, 0, stream, a);
   return hipGetLastError();
 }
 
