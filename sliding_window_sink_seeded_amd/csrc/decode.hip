@@ -109,8 +109,12 @@ struct KeyRows {
   }
 };
 
+// With one bf16 column block, asking for two waves per SIMD makes the compiler keep the
+// accumulators in VGPRs (169 registers, no AGPR copies) instead of 137 VGPRs + 80 AGPRs; both give
+// two waves per SIMD, the first runs faster (ring workload).
 template <typename E, int NCB, bool PREFETCH>
-__global__ __launch_bounds__(kDecNW * 64) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kDecNW * 64)
+__attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void decode_kernel(const DecodeArgs a) {
   using Frag = typename E::Frag;
   using Lds = DecodeLds<E, NCB>;
   __shared__ __attribute__((aligned(16))) char smem[Lds::kBytes];
