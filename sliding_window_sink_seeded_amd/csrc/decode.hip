@@ -123,7 +123,7 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
 
   const int split = blockIdx.x;
   const int g = blockIdx.y;
