@@ -241,7 +241,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
 
   // Heaviest query blocks (latest positions) are dispatched first.
   const int per_q = a.B * a.Hkv * a.n_hchunks;
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
 
   // workgroup -> (segment, head chunk, KV head, sequence); segments of one (b, g) are adjacent
   int rest = blockIdx.x;
