@@ -106,7 +106,8 @@ struct DecodePlan {
 };
 
 // Splits: one workgroup per (sequence, KV head) already fills the chip when there are >= 1024
-// pairs; otherwise split the longest key list so that about 2048 workgroups run, keeping each
+// pairs; otherwise split the longest key list so that about 1024 workgroups run (8 x 262144 keys,
+// 64/4 heads: 32 splits beat 16 and 64, measured), keeping each
 // split at >= 256 keys. An explicit request is honoured up to one 32-key block per split.
 DecodePlan plan_decode(int B, int T, int Hq, int Hkv, int max_len, int window, int num_splits) {
   DecodePlan p{};
@@ -121,7 +122,7 @@ DecodePlan plan_decode(int B, int T, int Hq, int Hkv, int max_len, int window, i
     ns = num_splits;
   } else {
     const long long pairs = (long long)B * Hkv;
-    ns = pairs >= 1024 ? 1 : (2048 + pairs - 1) / pairs;
+    ns = pairs >= 1024 ? 1 : (1024 + pairs - 1) / pairs;
     const long long cap = (list_max + 255) / 256;
     if (ns > cap) ns = cap;
   }

@@ -133,9 +133,9 @@ def test_workspace_size_query(lib):
     # single pass needs nothing
     assert mimo.decode_workspace_size(256, 4, 64, 8, 128, 32768, 128) == 0
     assert mimo.decode_workspace_size(256, 4, 64, 8, 128, 32768, 128, 1) == 0
-    # 8 sequences x 262144 keys, 64/4 heads: 64 splits of 4096 keys, records of 132 floats
+    # 8 sequences x 262144 keys, 64/4 heads: 32 splits of 8192 keys, records of 132 floats
     # (128 output values, running max and sum, two pad floats)
-    assert mimo.decode_workspace_size(8, 4, 64, 4, 128, 262144, 1 << 30) == 8 * 4 * 64 * 64 * 132 * 4
+    assert mimo.decode_workspace_size(8, 4, 64, 4, 128, 262144, 1 << 30) == 8 * 4 * 32 * 64 * 132 * 4
     assert mimo.decode_workspace_size(8, 4, 64, 4, 128, 262144, 1 << 30, 7) == 8 * 4 * 7 * 64 * 132 * 4
     # invalid arguments -> 0
     assert mimo.decode_workspace_size(8, 5, 64, 4, 128, 1000, 128) == 0
