@@ -38,7 +38,7 @@ struct DecodeArgs {
   const float* sink;
   void* o;
   float* lse;
-  float* ws;  // [B][Hkv][nsplit][ncols_pad][kDDV + 2] fp32 when nsplit > 1
+  float* ws;  // [B][Hkv][nsplit][ncols_pad][kDDV + 4] fp32 when nsplit > 1
   int B, T, Hq, Hkv, G, C;
   int max_len;
   int window;  // clamped to <= max_len + T by the host
