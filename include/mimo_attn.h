@@ -60,10 +60,12 @@ enum {
  *   sink  [Hq] fp32 device, nullable (NULL = no sink, same as every entry -inf)
  *   kv_head_of_q [Hq] int32 HOST array, nullable. NULL means h / (Hq/Hkv). Otherwise every KV head
  *         must serve exactly Hq/Hkv query heads; query heads of one KV head are processed together.
- *   window >= 1; window >= L selects global causal attention. scale multiplies q.k only.
+ *   window >= 1; window >= L selects global causal attention. scale multiplies q.k only and must
+ *   be finite and > 0 (the usual 1/sqrt(d_qk)).
  *
  * Errors: MIMO_EINVAL for B, L, Hq, Hkv < 1, Hq % Hkv != 0, a bad head map, window < 1, NULL or
- * misaligned q/k/v/o, misaligned sink/lse, non-finite scale, or tensors larger than 2^62 bytes;
+ * misaligned q/k/v/o, misaligned sink/lse, a scale that is not finite and > 0, or tensors larger
+ * than 2^62 bytes;
  * MIMO_EUNSUPPORTED for other head dims or dtypes; MIMO_EHIP if the launch fails.
  */
 int mimo_attn_prefill(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v,

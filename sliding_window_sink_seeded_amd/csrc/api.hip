@@ -53,7 +53,9 @@ int check_common(int dt, int B, int Hq, int Hkv, int d_qk, int d_v, int window, 
   if (Hq % Hkv) return fail(MIMO_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (Hq > mimo::kMaxHeads) return fail(MIMO_EUNSUPPORTED, "Hq %d exceeds %d", Hq, mimo::kMaxHeads);
   if (window < 1) return fail(MIMO_EINVAL, "window must be >= 1 (got %d)", window);
-  if (!std::isfinite(scale)) return fail(MIMO_EINVAL, "scale must be finite");
+  // the kernels scale the running max of raw scores, which equals the max of scaled scores only
+  // for a positive scale
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(MIMO_EINVAL, "scale must be finite and > 0");
   if (d_qk != 192 || d_v != 128)
     return fail(MIMO_EUNSUPPORTED, "head dims (%d, %d) unsupported; this build has (192, 128)", d_qk, d_v);
   return MIMO_OK;

@@ -72,6 +72,8 @@ def prefill(lib, dt=BF16, B=1, L=64, Hq=64, Hkv=8, dqk=192, dv=128, q=P, k=P, v=
     (dict(lse=ctypes.c_void_p(0x10001)), EINVAL),
     (dict(scale=float("nan")), EINVAL),
     (dict(scale=float("inf")), EINVAL),
+    (dict(scale=0.0), EINVAL),
+    (dict(scale=-0.07), EINVAL),
 ])
 def test_prefill_validation(lib, kw, code):
     assert prefill(lib, **kw) == code
@@ -114,6 +116,8 @@ def decode(lib, dt=BF16, B=4, T=4, Hq=64, Hkv=8, dqk=192, dv=128, q=P, kn=P, vn=
     (dict(offs=ctypes.c_void_p(0x10002)), EINVAL),
     (dict(dqk=64), EUNSUPPORTED),
     (dict(window=0), EINVAL),
+    (dict(scale=0.0), EINVAL),
+    (dict(scale=-0.07), EINVAL),
     (dict(window=10**9, C=512, max_len=1000), EINVAL),  # global cache smaller than the history
     (dict(window=10**9, C=1000, max_len=1000, B=2, Hkv=4, Hq=64, nsplit=4), EWORKSPACE),
 ])

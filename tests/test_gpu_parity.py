@@ -90,6 +90,20 @@ def test_prefill_sink_variants(dtype):
     np.testing.assert_allclose(lse, 1e4, rtol=1e-6)
 
 
+def test_prefill_global_sink_variants():
+    # the global-attention kernel seeds its running max from the sink like the ring kernel does
+    inp = prefill_inputs(17, 1, 190, 16, 2, 192, 128, 10**9, "bf16")
+    say("global prefill no sink")
+    check_prefill(inp, use_sink=False)
+    say("global prefill mixed sinks")
+    mixed = np.array([-np.inf, 0, 3, -3, 8, -20, 1, 2, 40, -np.inf, 0.5, 5, -1, 12, 0, 7], np.float32)
+    check_prefill(inp, sink=mixed)
+    say("global prefill dominant sinks")
+    o, lse, ref_o, ref_lse = run_prefill(inp, sink=np.full(16, 1e4, np.float32))
+    assert np.all(o == 0.0)
+    np.testing.assert_allclose(lse, 1e4, rtol=1e-6)
+
+
 def test_prefill_peaky_scores():
     say("prefill peaky")
     inp = prefill_inputs(16, 1, 200, 16, 2, 192, 128, 128, "bf16")
