@@ -12,7 +12,8 @@ timed steps. One JSON line goes to stdout, with:
   launch duration, timed with HIP events on the launch stream, against MI355X's published peak;
 * cpu_baseline - the float64 oracle timed on the host on a bounded leading slice of the same
   workload (a reported baseline, not a target);
-* secondary - the other measured workloads (global prefill, ring decode, split-KV global decode),
+* secondary - the other measured workloads (fp32 prefill, global prefill, ring decode, split-KV
+  global decode, and both decodes at the 16K-context / 64-sequence MTP setting),
   timed the same way, with decode inputs rotated over enough copies to defeat the 256 MiB MALL.
 """
 
@@ -345,7 +346,8 @@ def main():
 
     secondary = []
     if not args.no_secondary:
-        for name in ("swa_prefill_f32", "ga_prefill_bf16", "swa_decode_bf16", "ga_decode_bf16"):
+        for name in ("swa_prefill_f32", "ga_prefill_bf16", "swa_decode_bf16", "ga_decode_bf16",
+                     "swa_decode_mtp_bf16", "ga_decode_mtp_bf16"):
             if name == w.name:
                 continue
             c = Case(workloads.WORKLOADS[name])

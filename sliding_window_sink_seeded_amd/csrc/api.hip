@@ -107,10 +107,11 @@ struct DecodePlan {
   size_t ws_bytes;
 };
 
-// Splits: one workgroup per (sequence, KV head) already fills the chip when there are >= 1024
-// pairs; otherwise split the longest key list so that about 1024 workgroups run (8 x 262144 keys,
-// 64/4 heads: 32 splits beat 16 and 64, measured), keeping each
-// split at >= 256 keys. An explicit request is honoured up to one 32-key block per split.
+// Splits: about 8192 committed keys per split, but at least one workgroup per compute unit of an
+// MI355X (256), and never fewer than 256 keys per split. Sweeps of explicit split counts: 8 x 262144
+// keys (64/4 heads) 16: 968 us, 32: 951 us, 64: 981 us, 128: 1082 us; 64 x 16384 keys 1: 552 us,
+// 2: 493 us, 4: 515 us, 8: 558 us; 64 x 127 ring keys 1: 17 us, 2: 32 us. An explicit request is
+// honoured up to one 32-key block per split.
 DecodePlan plan_decode(int B, int T, int Hq, int Hkv, int max_len, int window, int num_splits) {
   DecodePlan p{};
   const long long wmax = (long long)max_len + T;
@@ -124,7 +125,9 @@ DecodePlan plan_decode(int B, int T, int Hq, int Hkv, int max_len, int window, i
     ns = num_splits;
   } else {
     const long long pairs = (long long)B * Hkv;
-    ns = pairs >= 1024 ? 1 : (1024 + pairs - 1) / pairs;
+    const long long fill = (256 + pairs - 1) / pairs;
+    const long long by_len = (list_max + 8191) / 8192;
+    ns = fill > by_len ? fill : by_len;
     const long long cap = (list_max + 255) / 256;
     if (ns > cap) ns = cap;
   }

@@ -1,4 +1,4 @@
-"""The five measured workloads and their algorithmic work.
+"""The measured workloads and their algorithmic work.
 
 Shapes follow the MiMo-V2-Flash Technical Report review (xllm-io), §3.1: window 128; 64 query heads
 over 8 KV heads for sliding-window layers and over 4 KV heads for global layers; Q/K head dim 192,
@@ -64,6 +64,17 @@ WORKLOADS = {
     "ga_decode_bf16": Workload(
         "ga_decode_bf16", "decode", "bf16", 64, 4, 1 << 30, B=8, T=4, C=262144, P=262144, seed=5,
         description="global decode bf16, 8 seqs x 262144 cached + 4 tokens, 64/4 heads, split-KV"),
+    # The pages' own MTP measurement setting: 16K-token inputs, 64 sequences per node, 1 + 3
+    # drafts verified per step (MiMo-V2-Flash Technical Report review (xllm-io), §6.3; MiMo series
+    # notes (plmsmile), MiMo-V2-Flash paper summary > evaluation and system experiments, and > MTP
+    # decode gains).
+    "swa_decode_mtp_bf16": Workload(
+        "swa_decode_mtp_bf16", "decode", "bf16", 64, 8, 128, B=64, T=4, C=128, P=16384,
+        ring_offsets=True, seed=6,
+        description="sliding-window decode bf16, 64 seqs x 16384 cached + 4 tokens, 128-slot ring, 64/8 heads"),
+    "ga_decode_mtp_bf16": Workload(
+        "ga_decode_mtp_bf16", "decode", "bf16", 64, 4, 1 << 30, B=64, T=4, C=16384, P=16384, seed=7,
+        description="global decode bf16, 64 seqs x 16384 cached + 4 tokens, 64/4 heads, split-KV"),
 }
 
 
