@@ -13,7 +13,8 @@ timed steps. One JSON line goes to stdout, with:
 * cpu_baseline - the float64 oracle timed on the host on a bounded leading slice of the same
   workload (a reported baseline, not a target);
 * secondary - the other measured workloads (fp32 prefill, global prefill, ring decode, split-KV
-  global decode, and both decodes at the 16K-context / 64-sequence MTP setting),
+  global decode, both decodes at the 16K-context / 64-sequence MTP setting, and the four bf16
+  workloads with the rotary embedding fused),
   timed the same way, with decode inputs rotated over enough copies to defeat the 256 MiB MALL.
 """
 
@@ -73,6 +74,10 @@ class Case:
         if rotate_to_defeat_mall and self.bytes < 4 * MALL_BYTES:
             n_sets = min(16, max(2, math.ceil(8 * MALL_BYTES / self.bytes)))
         self.sink = torch.from_numpy(self.inp.sink).cuda()
+        self.rope = None
+        if w.rope_base > 0:  # built once, outside the timed region, like a model's cos/sin cache
+            n_pos = w.L if w.kind == "prefill" else int(w.P or w.len_range[1]) + w.T
+            self.rope = mimo.rope_table(n_pos, w.rope_base)
         self.sets = []
         if w.kind == "prefill":
             base = [up(self.inp.q), up(self.inp.k), up(self.inp.v)]
@@ -102,11 +107,12 @@ class Case:
         self.i += 1
         w = self.w
         if w.kind == "prefill":
-            self.mimo.prefill(ts[0], ts[1], ts[2], w.window, sink=self.sink, scale=self.inp.scale, out=o)
+            self.mimo.prefill(ts[0], ts[1], ts[2], w.window, sink=self.sink, scale=self.inp.scale, out=o,
+                              rope=self.rope)
         else:
             self.mimo.decode(ts[0], ts[1], ts[2], ts[3], ts[4], self.len_t, w.window, self.max_len,
                              cache_offset=self.off_t, sink=self.sink, scale=self.inp.scale,
-                             workspace=self.ws, out=o)
+                             workspace=self.ws, out=o, rope=self.rope)
         return o
 
     def time(self, steps, warmup, min_warm_s=0.25):
@@ -347,7 +353,8 @@ def main():
     secondary = []
     if not args.no_secondary:
         for name in ("swa_prefill_f32", "ga_prefill_bf16", "swa_decode_bf16", "ga_decode_bf16",
-                     "swa_decode_mtp_bf16", "ga_decode_mtp_bf16"):
+                     "swa_decode_mtp_bf16", "ga_decode_mtp_bf16", "swa_prefill_rope_bf16",
+                     "ga_prefill_rope_bf16", "swa_decode_rope_bf16", "ga_decode_rope_bf16"):
             if name == w.name:
                 continue
             c = Case(workloads.WORKLOADS[name])

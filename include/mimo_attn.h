@@ -114,6 +114,49 @@ int mimo_attn_decode(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int
                      void* workspace, size_t workspace_bytes, void* o, float* lse,
                      hipStream_t stream);
 
+/*
+ * Rotary position embedding of the leading Q/K dimensions (MiMo-V2-Flash Technical Report review
+ * (xllm-io), §3.1: RoPE on the first 64 of the 192 Q/K dims; §4: base 10K for the sliding-window
+ * layers, 5M for the global layers). The rot_dims leading dims of a head vector at position p form
+ * pairs (i, i + rot_dims/2), i < rot_dims/2, rotated by a = p * base^(-2i / rot_dims):
+ *     x' = x cos a - y sin a,   y' = y cos a + x sin a;
+ * the other dims and V are not rotated. Only rot_dims = 64 is implemented.
+ *
+ * mimo_attn_rope_table fills `table` [n_pos][rot_dims/2][2] fp32 (device, caller-owned) with
+ * (cos a, sin a) for positions 0 .. n_pos-1, evaluated in fp64 on the device and rounded to fp32.
+ * Errors: MIMO_EINVAL for n_pos outside [1, 2^30], base not finite or <= 1, NULL or misaligned
+ * table; MIMO_EUNSUPPORTED for rot_dims != 64; MIMO_EHIP if the launch fails.
+ */
+int mimo_attn_rope_table(int n_pos, int rot_dims, double base, float* table, hipStream_t stream);
+
+/*
+ * mimo_attn_prefill for q and k given BEFORE the rotary embedding: every Q and K head vector of row
+ * i is rotated by position i with rope_table (rope_positions >= L rows from mimo_attn_rope_table)
+ * before the dot products; in bf16 the rotated values are rounded to bf16 (nearest even) first.
+ * Other arguments and errors as mimo_attn_prefill; additionally MIMO_EINVAL for a NULL or
+ * misaligned table or rope_positions < L, MIMO_EUNSUPPORTED for rot_dims != 64.
+ */
+int mimo_attn_prefill_rope(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v,
+                           const void* q, const void* k, const void* v, int window,
+                           const float* sink, const int32_t* kv_head_of_q, float scale,
+                           const float* rope_table, int rope_positions, int rot_dims, void* o,
+                           float* lse, hipStream_t stream);
+
+/*
+ * mimo_attn_decode for q and k_new given BEFORE the rotary embedding: new token t of sequence b is
+ * rotated by position P_b + t (rope_positions >= max_cache_len + T); the cache is expected to hold
+ * keys that were rotated when their tokens were processed. Other arguments and errors as
+ * mimo_attn_decode (same workspace size), plus the table checks of mimo_attn_prefill_rope.
+ */
+int mimo_attn_decode_rope(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
+                          const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                          const void* v_cache, int C, const int32_t* cache_len,
+                          const int32_t* cache_offset, int max_cache_len, int window,
+                          const float* sink, const int32_t* kv_head_of_q, float scale,
+                          const float* rope_table, int rope_positions, int rot_dims,
+                          int num_splits, void* workspace, size_t workspace_bytes, void* o,
+                          float* lse, hipStream_t stream);
+
 /* Thread-local description of the last non-zero return on this thread ("" if none). */
 const char* mimo_attn_last_error(void);
 

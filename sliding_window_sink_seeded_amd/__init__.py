@@ -7,6 +7,8 @@ fallback. If the shared library is missing, every call raises.
 
     o, lse = prefill(q, k, v, window=128, sink=sink)          # q [B, L, Hq, 192] ...
     o, lse = decode(q, k_new, v_new, k_cache, v_cache, cache_len, window=128, ...)
+    table = rope_table(n_pos, base=1e4)                        # RoPE (cos, sin), device fp32
+    o, lse = prefill(q, k, v, 128, sink=sink, rope=table)      # q, k given before RoPE
 """
 
 from __future__ import annotations
@@ -15,12 +17,14 @@ import ctypes
 import math
 import os
 
-__all__ = ["prefill", "decode", "decode_workspace_size", "last_error", "version", "library",
-           "LIB_PATH", "MimoError", "EXPORTS"]
+__all__ = ["prefill", "decode", "decode_workspace_size", "rope_table", "last_error", "version",
+           "library", "LIB_PATH", "MimoError", "EXPORTS", "ROPE_DIMS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmimo_attn.so")
 EXPORTS = ("mimo_attn_prefill", "mimo_attn_decode", "mimo_attn_decode_workspace_size",
+           "mimo_attn_rope_table", "mimo_attn_prefill_rope", "mimo_attn_decode_rope",
            "mimo_attn_last_error", "mimo_attn_version")
+ROPE_DIMS = 64  # rotated leading Q/K dims
 
 MIMO_F32, MIMO_BF16 = 0, 1
 _CODES = {-1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP"}
@@ -52,6 +56,15 @@ def library() -> ctypes.CDLL:
     lib.mimo_attn_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp,
                                      vp, i32, i32, vp, vp, f32, i32, vp, sz, vp, vp, vp]
     lib.mimo_attn_decode.restype = i32
+    lib.mimo_attn_rope_table.argtypes = [i32, i32, ctypes.c_double, vp, vp]
+    lib.mimo_attn_rope_table.restype = i32
+    lib.mimo_attn_prefill_rope.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp,
+                                           vp, f32, vp, i32, i32, vp, vp, vp]
+    lib.mimo_attn_prefill_rope.restype = i32
+    lib.mimo_attn_decode_rope.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                          i32, vp, vp, i32, i32, vp, vp, f32, vp, i32, i32, i32, vp,
+                                          sz, vp, vp, vp]
+    lib.mimo_attn_decode_rope.restype = i32
     lib.mimo_attn_last_error.argtypes = []
     lib.mimo_attn_last_error.restype = ctypes.c_char_p
     lib.mimo_attn_version.argtypes = []
@@ -115,12 +128,36 @@ def _kv_map(kv_map, Hq):
     return arr, ctypes.cast(arr, ctypes.c_void_p)
 
 
+def rope_table(n_pos: int, base: float, out=None, stream=None):
+    """(cos, sin) table [n_pos, 32, 2] fp32 of the rotary angles, filled by the library kernel."""
+    import torch
+
+    if out is None:
+        out = torch.empty((n_pos, ROPE_DIMS // 2, 2), dtype=torch.float32, device="cuda")
+    _dev(out, "out", torch.float32, 3)
+    if tuple(out.shape) != (n_pos, ROPE_DIMS // 2, 2):
+        raise ValueError("out has the wrong shape")
+    _check(library().mimo_attn_rope_table(int(n_pos), ROPE_DIMS, float(base), _ptr(out),
+                                          _stream(stream)))
+    return out
+
+
+def _rope_arg(rope):
+    import torch
+
+    _dev(rope, "rope", torch.float32, 3)
+    if tuple(rope.shape[1:]) != (ROPE_DIMS // 2, 2):
+        raise ValueError("rope must be a [n_pos, 32, 2] table from rope_table()")
+    return rope.shape[0]
+
+
 def prefill(q, k, v, window: int, sink=None, scale: float | None = None, kv_map=None, out=None,
-            lse=None, return_lse: bool = False, stream=None):
+            lse=None, return_lse: bool = False, stream=None, rope=None):
     """Sink-seeded windowed prefill. q [B, L, Hq, dqk], k [B, L, Hkv, dqk], v [B, L, Hkv, dv].
 
     window >= L means global causal attention. sink: fp32 [Hq] GPU tensor or None. kv_map: host
-    sequence of Hq KV-head indices (None = contiguous groups). Returns (o, lse or None).
+    sequence of Hq KV-head indices (None = contiguous groups). rope: None, or a table from
+    rope_table() when q and k are given before the rotary embedding. Returns (o, lse or None).
     """
     import torch
 
@@ -150,9 +187,16 @@ def prefill(q, k, v, window: int, sink=None, scale: float | None = None, kv_map=
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
     keep, kvm = _kv_map(kv_map, Hq)
-    rc = library().mimo_attn_prefill(dt, B, L, Hq, Hkv, dqk, dv, _ptr(q), _ptr(k), _ptr(v),
-                                     int(window), _ptr(sink), kvm, float(scale), _ptr(out),
-                                     _ptr(lse), _stream(stream))
+    if rope is None:
+        rc = library().mimo_attn_prefill(dt, B, L, Hq, Hkv, dqk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                         int(window), _ptr(sink), kvm, float(scale), _ptr(out),
+                                         _ptr(lse), _stream(stream))
+    else:
+        n_pos = _rope_arg(rope)
+        rc = library().mimo_attn_prefill_rope(dt, B, L, Hq, Hkv, dqk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                              int(window), _ptr(sink), kvm, float(scale), _ptr(rope),
+                                              int(n_pos), ROPE_DIMS, _ptr(out), _ptr(lse),
+                                              _stream(stream))
     del keep
     _check(rc)
     return out, lse
@@ -166,11 +210,13 @@ def decode_workspace_size(B, T, Hq, Hkv, dv, max_cache_len, window, num_splits=0
 def decode(q, k_new, v_new, k_cache, v_cache, cache_len, window: int, max_cache_len: int,
            cache_offset=None, sink=None, scale: float | None = None, kv_map=None,
            num_splits: int = 0, workspace=None, out=None, lse=None, return_lse: bool = False,
-           stream=None):
+           stream=None, rope=None):
     """Decode / MTP verify of T = q.shape[1] new tokens per sequence.
 
     q [B, T, Hq, dqk]; k_new/v_new [B, T, Hkv, d]; k_cache/v_cache [B, C, Hkv, d];
-    cache_len / cache_offset int32 [B] GPU tensors. Returns (o, lse or None).
+    cache_len / cache_offset int32 [B] GPU tensors. rope: None, or a table from rope_table() when
+    q and k_new are given before the rotary embedding (the cache holds rotated keys). Returns
+    (o, lse or None).
     """
     import torch
 
@@ -202,11 +248,21 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_len, window: int, max_cache_
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     keep, kvm = _kv_map(kv_map, Hq)
-    rc = library().mimo_attn_decode(dt, B, T, Hq, Hkv, dqk, dv, _ptr(q), _ptr(k_new), _ptr(v_new),
-                                    _ptr(k_cache), _ptr(v_cache), C, _ptr(cache_len),
-                                    _ptr(cache_offset), int(max_cache_len), int(window), _ptr(sink),
-                                    kvm, float(scale), int(num_splits), _ptr(workspace), ws_have,
-                                    _ptr(out), _ptr(lse), _stream(stream))
+    if rope is None:
+        rc = library().mimo_attn_decode(dt, B, T, Hq, Hkv, dqk, dv, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                        _ptr(k_cache), _ptr(v_cache), C, _ptr(cache_len),
+                                        _ptr(cache_offset), int(max_cache_len), int(window),
+                                        _ptr(sink), kvm, float(scale), int(num_splits),
+                                        _ptr(workspace), ws_have, _ptr(out), _ptr(lse),
+                                        _stream(stream))
+    else:
+        n_pos = _rope_arg(rope)
+        rc = library().mimo_attn_decode_rope(dt, B, T, Hq, Hkv, dqk, dv, _ptr(q), _ptr(k_new),
+                                             _ptr(v_new), _ptr(k_cache), _ptr(v_cache), C,
+                                             _ptr(cache_len), _ptr(cache_offset), int(max_cache_len),
+                                             int(window), _ptr(sink), kvm, float(scale), _ptr(rope),
+                                             int(n_pos), ROPE_DIMS, int(num_splits), _ptr(workspace),
+                                             ws_have, _ptr(out), _ptr(lse), _stream(stream))
     del keep
     _check(rc)
     return out, lse

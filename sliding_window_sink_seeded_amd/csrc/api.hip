@@ -69,10 +69,15 @@ const char* mimo_attn_last_error(void) { return g_err.c_str(); }
 
 int mimo_attn_version(void) { return 10000; }
 
-int mimo_attn_prefill(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v,
-                      const void* q, const void* k, const void* v, int window, const float* sink,
-                      const int32_t* kv_head_of_q, float scale, void* o, float* lse,
-                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// rope: NULL, or a table of at least L positions for Q/K given before the rotary embedding
+int prefill_impl(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v, const void* q,
+                 const void* k, const void* v, int window, const float* sink,
+                 const int32_t* kv_head_of_q, float scale, const float* rope, void* o, float* lse,
+                 hipStream_t stream) {
   g_err.clear();
   if (int rc = check_common(dt, B, Hq, Hkv, d_qk, d_v, window, scale)) return rc;
   if (L < 1) return fail(MIMO_EINVAL, "L must be >= 1");
@@ -86,13 +91,59 @@ int mimo_attn_prefill(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, in
   if ((double)B * L * Hq * d_qk * elem > 4.6e18) return fail(MIMO_EINVAL, "tensor too large");
 
   mimo::PrefillArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.sink = sink;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.sink = sink; a.rope = rope;
   a.B = B; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
   a.window = window < L ? window : L;
   a.scale_log2 = scale * mimo::kLog2e;
   if (int rc = group_heads(Hq, Hkv, kv_head_of_q, &a.hl)) return rc;
   const hipError_t e = mimo::prefill_launch(dt == MIMO_BF16, a, stream);
   if (e != hipSuccess) return fail(MIMO_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return MIMO_OK;
+}
+
+int check_rope(const float* table, int positions, int rot_dims, long long need) {
+  if (rot_dims != mimo::kRopeDims)
+    return fail(MIMO_EUNSUPPORTED, "rot_dims %d unsupported; this build rotates %d dims", rot_dims,
+                mimo::kRopeDims);
+  if (!table || !aligned16(table)) return fail(MIMO_EINVAL, "rope_table must be non-NULL and 16-byte aligned");
+  if (positions < need)
+    return fail(MIMO_EINVAL, "rope_table has %d positions, %lld needed", positions, need);
+  return MIMO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mimo_attn_prefill(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v,
+                      const void* q, const void* k, const void* v, int window, const float* sink,
+                      const int32_t* kv_head_of_q, float scale, void* o, float* lse,
+                      hipStream_t stream) {
+  return prefill_impl(dt, B, L, Hq, Hkv, d_qk, d_v, q, k, v, window, sink, kv_head_of_q, scale,
+                      nullptr, o, lse, stream);
+}
+
+int mimo_attn_prefill_rope(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v,
+                           const void* q, const void* k, const void* v, int window,
+                           const float* sink, const int32_t* kv_head_of_q, float scale,
+                           const float* rope_table, int rope_positions, int rot_dims, void* o,
+                           float* lse, hipStream_t stream) {
+  g_err.clear();
+  if (int rc = check_rope(rope_table, rope_positions, rot_dims, L)) return rc;
+  return prefill_impl(dt, B, L, Hq, Hkv, d_qk, d_v, q, k, v, window, sink, kv_head_of_q, scale,
+                      rope_table, o, lse, stream);
+}
+
+int mimo_attn_rope_table(int n_pos, int rot_dims, double base, float* table, hipStream_t stream) {
+  g_err.clear();
+  if (rot_dims != mimo::kRopeDims)
+    return fail(MIMO_EUNSUPPORTED, "rot_dims %d unsupported; this build rotates %d dims", rot_dims,
+                mimo::kRopeDims);
+  if (n_pos < 1 || n_pos > (1 << 30)) return fail(MIMO_EINVAL, "n_pos %d outside [1, 2^30]", n_pos);
+  if (!std::isfinite(base) || !(base > 1.0)) return fail(MIMO_EINVAL, "base must be finite and > 1");
+  if (!table || !aligned16(table)) return fail(MIMO_EINVAL, "table must be non-NULL and 16-byte aligned");
+  const hipError_t e = mimo::rope_table_launch(n_pos, base, table, stream);
+  if (e != hipSuccess) return fail(MIMO_EHIP, "rope table launch failed: %s", hipGetErrorString(e));
   return MIMO_OK;
 }
 
@@ -153,14 +204,17 @@ size_t mimo_attn_decode_workspace_size(int B, int T, int Hq, int Hkv, int d_v, i
   return plan_decode(B, T, Hq, Hkv, max_cache_len, window, num_splits).ws_bytes;
 }
 
-int mimo_attn_decode(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
-                     const void* q, const void* k_new, const void* v_new, const void* k_cache,
-                     const void* v_cache, int C, const int32_t* cache_len,
-                     const int32_t* cache_offset, int max_cache_len, int window,
-                     const float* sink, const int32_t* kv_head_of_q, float scale, int num_splits,
-                     void* workspace, size_t workspace_bytes, void* o, float* lse,
-                     hipStream_t stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// rope: NULL, or a table of at least max_cache_len + T positions for unrotated q / k_new
+int decode_impl(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v, const void* q,
+                const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
+                int C, const int32_t* cache_len, const int32_t* cache_offset, int max_cache_len,
+                int window, const float* sink, const int32_t* kv_head_of_q, float scale,
+                const float* rope, int num_splits, void* workspace, size_t workspace_bytes,
+                void* o, float* lse, hipStream_t stream) {
   if (int rc = check_common(dt, B, Hq, Hkv, d_qk, d_v, window, scale)) return rc;
   if (T < 1 || T > 4) return fail(MIMO_EINVAL, "T must be in 1..4 (got %d)", T);
   if ((Hq / Hkv) * T > mimo::kMaxCols)
@@ -195,7 +249,7 @@ int mimo_attn_decode(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int
 
   mimo::DecodeArgs a{};
   a.q = q; a.k_new = k_new; a.v_new = v_new; a.k_cache = k_cache; a.v_cache = v_cache;
-  a.cache_len = cache_len; a.cache_offset = cache_offset; a.sink = sink;
+  a.cache_len = cache_len; a.cache_offset = cache_offset; a.sink = sink; a.rope = rope;
   a.o = o; a.lse = lse; a.ws = static_cast<float*>(workspace);
   a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.C = C;
   a.max_len = max_cache_len;
@@ -208,6 +262,38 @@ int mimo_attn_decode(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int
   const hipError_t e = mimo::decode_launch(dt == MIMO_BF16, a, stream);
   if (e != hipSuccess) return fail(MIMO_EHIP, "decode launch failed: %s", hipGetErrorString(e));
   return MIMO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mimo_attn_decode(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
+                     const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                     const void* v_cache, int C, const int32_t* cache_len,
+                     const int32_t* cache_offset, int max_cache_len, int window,
+                     const float* sink, const int32_t* kv_head_of_q, float scale, int num_splits,
+                     void* workspace, size_t workspace_bytes, void* o, float* lse,
+                     hipStream_t stream) {
+  g_err.clear();
+  return decode_impl(dt, B, T, Hq, Hkv, d_qk, d_v, q, k_new, v_new, k_cache, v_cache, C, cache_len,
+                     cache_offset, max_cache_len, window, sink, kv_head_of_q, scale, nullptr,
+                     num_splits, workspace, workspace_bytes, o, lse, stream);
+}
+
+int mimo_attn_decode_rope(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
+                          const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                          const void* v_cache, int C, const int32_t* cache_len,
+                          const int32_t* cache_offset, int max_cache_len, int window,
+                          const float* sink, const int32_t* kv_head_of_q, float scale,
+                          const float* rope_table, int rope_positions, int rot_dims,
+                          int num_splits, void* workspace, size_t workspace_bytes, void* o,
+                          float* lse, hipStream_t stream) {
+  g_err.clear();
+  if (int rc = check_rope(rope_table, rope_positions, rot_dims, (long long)max_cache_len + T)) return rc;
+  return decode_impl(dt, B, T, Hq, Hkv, d_qk, d_v, q, k_new, v_new, k_cache, v_cache, C, cache_len,
+                     cache_offset, max_cache_len, window, sink, kv_head_of_q, scale, rope_table,
+                     num_splits, workspace, workspace_bytes, o, lse, stream);
 }
 
 }  // extern "C"

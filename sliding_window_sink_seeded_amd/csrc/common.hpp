@@ -202,6 +202,64 @@ __device__ __forceinline__ bf16x8 vt_frag_tr(const char* vtile, int row_elems, i
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// ---- rotary embedding of the leading 64 Q/K dims: pairs (i, i + 32) rotated by (cos, sin) of
+// position * base^(-2i/64), read from a [position][32][2] fp32 table ----
+constexpr int kRopeDims = 64;
+
+// cs[2j], cs[2j+1] = cos, sin for element j of `lo`; lo holds dims i0.., hi the partner dims
+// i0 + 32..; bf16 chunks carry 8 elements, fp32 chunks 4. Rotated values are rounded back to the
+// storage type (bf16: round to nearest even).
+template <typename E>
+__device__ __forceinline__ void rope_rotate_chunk(u32x4& lo, u32x4& hi, const float* cs) {
+  if constexpr (E::kBytes == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float x0 = __uint_as_float(lo[w] << 16), x1 = __uint_as_float(lo[w] & 0xFFFF0000u);
+      const float y0 = __uint_as_float(hi[w] << 16), y1 = __uint_as_float(hi[w] & 0xFFFF0000u);
+      const float c0 = cs[4 * w], s0 = cs[4 * w + 1], c1 = cs[4 * w + 2], s1 = cs[4 * w + 3];
+      lo[w] = pack_bf16x2(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+      hi[w] = pack_bf16x2(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float x = __uint_as_float(lo[w]), y = __uint_as_float(hi[w]);
+      const float c = cs[2 * w], s = cs[2 * w + 1];
+      lo[w] = __float_as_uint(x * c - y * s);
+      hi[w] = __float_as_uint(y * c + x * s);
+    }
+  }
+}
+
+// Loads n (cos, sin) pairs, n a multiple of 2, for dims i0 .. i0 + n - 1 at table row `pos`.
+template <int N>
+__device__ __forceinline__ void rope_load(const float* table, int pos, int i0, float (&cs)[2 * N]) {
+  const float* p = table + ((size_t)pos * (kRopeDims / 2) + i0) * 2;
+#pragma unroll
+  for (int j = 0; j < N / 2; ++j) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p + 4 * j);
+    cs[4 * j] = v[0]; cs[4 * j + 1] = v[1]; cs[4 * j + 2] = v[2]; cs[4 * j + 3] = v[3];
+  }
+}
+
+// Rotates an MFMA fragment pair (8 elements of dims i0.. and of dims i0 + 32..) in place.
+template <typename E, typename F>
+__device__ __forceinline__ void rope_rotate_frag(F& lo, F& hi, const float (&cs)[16]) {
+  if constexpr (E::kBytes == 2) {
+    u32x4 a = __builtin_bit_cast(u32x4, lo), b = __builtin_bit_cast(u32x4, hi);
+    rope_rotate_chunk<E>(a, b, cs);
+    lo = __builtin_bit_cast(F, a);
+    hi = __builtin_bit_cast(F, b);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = lo[e], y = hi[e], c = cs[2 * e], s = cs[2 * e + 1];
+      lo[e] = x * c - y * s;
+      hi[e] = y * c + x * s;
+    }
+  }
+}
+
 template <bool B>
 struct BoolTag {
   static constexpr bool value = B;

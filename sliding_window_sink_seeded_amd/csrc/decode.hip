@@ -112,7 +112,7 @@ struct KeyRows {
 // With one bf16 column block, asking for two waves per SIMD makes the compiler keep the
 // accumulators in VGPRs (169 registers, no AGPR copies) instead of 137 VGPRs + 80 AGPRs; both give
 // two waves per SIMD, the first runs faster (ring workload).
-template <typename E, int NCB, bool PREFETCH>
+template <typename E, int NCB, bool PREFETCH, bool ROPE>
 __global__ __launch_bounds__(kDecNW * 64)
 __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void decode_kernel(const DecodeArgs a) {
   using Frag = typename E::Frag;
@@ -255,6 +255,34 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
   char* work = smem + Lds::kQBytes + Lds::kNewBytes;
   char* my_vt = work + wave * Lds::kVBytes;
   __syncthreads();  // Q^T and the new-token rows are in LDS
+
+  if constexpr (ROPE) {
+    // q and k_new arrive before the rotary embedding: rotate them in LDS, query column c (token
+    // c % T) and new token t at positions P + c % T and P + t; pairs (i, i + 32), i < 32
+    constexpr int kHalfRot = kRopeDims / 2;
+    const bool last = split == a.nsplit - 1;
+    const int n_q = a.ncols * kHalfRot, n_k = last ? a.T * kHalfRot : 0;
+    for (int u = tid; u < n_q + n_k; u += kDecNW * 64) {
+      const bool is_q = u < n_q;
+      const int uu = is_q ? u : u - n_q;
+      const int row = uu / kHalfRot, i = uu % kHalfRot;
+      const int pos = P + (is_q ? row % a.T : row);
+      char* base = is_q ? sq + row * Lds::kQStride * E::kBytes : smem + Lds::kQBytes + row * kDDQK * E::kBytes;
+      const f32x2 csn = *reinterpret_cast<const f32x2*>(a.rope + ((size_t)pos * kHalfRot + i) * 2);
+      if constexpr (E::kBytes == 2) {
+        uint16_t* e = reinterpret_cast<uint16_t*>(base);
+        const float x = __uint_as_float((uint32_t)e[i] << 16), y = __uint_as_float((uint32_t)e[i + kHalfRot] << 16);
+        e[i] = (uint16_t)bf16_bits(x * csn[0] - y * csn[1]);
+        e[i + kHalfRot] = (uint16_t)bf16_bits(y * csn[0] + x * csn[1]);
+      } else {
+        float* e = reinterpret_cast<float*>(base);
+        const float x = e[i], y = e[i + kHalfRot];
+        e[i] = x * csn[0] - y * csn[1];
+        e[i + kHalfRot] = y * csn[0] + x * csn[1];
+      }
+    }
+    __syncthreads();
+  }
 
   for (; key0 < s1; key0 += 32 * kDecNW) {
     cur.store_v(my_vt, col, half);
@@ -566,18 +594,26 @@ size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit) {
 #define MIMO_DECODE_PREFETCH_1COL false
 #endif
 
-hipError_t decode_launch(bool bf16, const DecodeArgs& a, hipStream_t stream) {
+template <bool ROPE>
+static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
   const dim3 block(kDecNW * 64);
   const bool two = a.ncols > 32;
   if (bf16 && two)
-    hipLaunchKernelGGL((decode_kernel<BF16, 2, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<BF16, 2, true, ROPE>), grid, block, 0, stream, a);
   else if (bf16)
-    hipLaunchKernelGGL((decode_kernel<BF16, 1, MIMO_DECODE_PREFETCH_1COL>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<BF16, 1, MIMO_DECODE_PREFETCH_1COL, ROPE>), grid, block, 0, stream, a);
   else if (two)
-    hipLaunchKernelGGL((decode_kernel<F32, 2, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<F32, 2, false, ROPE>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<F32, 1, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<F32, 1, false, ROPE>), grid, block, 0, stream, a);
+}
+
+hipError_t decode_launch(bool bf16, const DecodeArgs& a, hipStream_t stream) {
+  if (a.rope)
+    launch_decode_kernel<true>(bf16, a, stream);
+  else
+    launch_decode_kernel<false>(bf16, a, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const dim3 cgrid((a.ncols + kCombCols - 1) / kCombCols, a.Hkv, a.B);

@@ -23,6 +23,7 @@ struct PrefillArgs {
   int n_hchunks;     // G / HG
   int n_segments;    // sliding-window ring kernel: segments of consecutive tiles per (b, g, chunk)
   int tiles_per_wg;  // sliding-window ring kernel: 32-row tiles per segment
+  const float* rope;  // [>= L][32][2] (cos, sin) when Q/K arrive before the rotary embedding, else NULL
   HeadList hl;
 };
 
@@ -46,9 +47,12 @@ struct DecodeArgs {
   int nsplit;
   int keys_per_split;  // multiple of 32
   int ncols;           // G * T
+  const float* rope;   // [>= max_len + T][32][2] (cos, sin) when q/k_new arrive unrotated, else NULL
   HeadList hl;
 };
 
+// Fills table[p][i] = (cos, sin)(p * base^(-2i/64)), p < n_pos, i < 32, evaluated in fp64.
+hipError_t rope_table_launch(int n_pos, double base, float* table, hipStream_t stream);
 // Picks the prefill variant (fills the tiling fields of `a`) and launches it on `stream`.
 hipError_t prefill_launch(bool bf16, PrefillArgs a, hipStream_t stream);
 // Launches the decode kernel and, when a.nsplit > 1, the combine kernel on `stream`.

@@ -53,13 +53,26 @@ struct PrefillTile {
 // t + i * NT with key = chunk % BK, so a wave's lanes cover consecutive keys of one dv range and
 // its 4-byte transposed writes hit distinct banks.
 // Rows at or past L are read from row L - 1 (finite data that the mask gives weight 0).
-template <typename E, int NT, int BK>
+//
+// ROPE: K arrives before the rotary embedding. Thread j < H of a K row (H = chunks per 32 dims)
+// then holds the partner chunks j and j + H (dims 8j.. and 8j + 32.. for bf16) plus KPT - 2 chunks
+// of the unrotated dims, the other threads KPT chunks of the rest; load() also fetches the
+// (cos, sin) pairs of its key position and store() rotates the pair before writing LDS.
+template <typename E, int NT, int BK, bool ROPE = false>
 struct KVStager {
   using Tile = PrefillTile<E, BK>;
   static constexpr int kKChunksRow = kDQK / E::kPerChunk;
   static constexpr int KPT = (BK * kKChunksRow + NT - 1) / NT;  // K chunks per thread
   static_assert(kKChunksRow % KPT == 0, "a thread's K chunks stay in one row");
   static constexpr int kKTpr = kKChunksRow / KPT;  // threads per K row
+  static constexpr int H = kRopeDims / 2 / E::kPerChunk;  // chunks in 32 dims
+  static_assert(!ROPE || (KPT >= 2 && kKTpr >= H), "each rotated chunk pair fits one thread");
+  // chunk (within the row) of this thread's i-th K chunk; j = thread index within the row
+  __device__ static constexpr int kchunk(int j, int i) {
+    if (!ROPE) return j * KPT + i;
+    if (j < H) return i == 0 ? j : (i == 1 ? j + H : 2 * H + j * (KPT - 2) + (i - 2));
+    return 2 * H + H * (KPT - 2) + (j - H) * KPT + i;
+  }
   static constexpr int kKActive = BK * kKTpr;
   static_assert(kKActive <= NT, "one pass covers the K block");
   static constexpr int kVChunksRow = kDV / E::kPerChunk;
@@ -72,10 +85,11 @@ struct KVStager {
   u32x4 vr[VPT];
   uint32_t koff, voff[Tile::kVRowMajor ? 1 : VPT];
   int krow, vrow;
+  float cs[ROPE ? 2 * E::kPerChunk : 1];  // (cos, sin) of this thread's rotated dims
 
   __device__ __forceinline__ void init(size_t kstride, size_t vstride, int tid) {
     krow = min(tid / kKTpr, BK - 1);
-    koff = (uint32_t)(krow * kstride + (tid % kKTpr) * KPT * 16);
+    koff = ROPE ? (uint32_t)(krow * kstride) : (uint32_t)(krow * kstride + (tid % kKTpr) * KPT * 16);
     if constexpr (Tile::kVRowMajor) {
       vrow = min(tid / kVTpr, BK - 1);
       voff[0] = (uint32_t)(vrow * vstride + (tid % kVTpr) * VPT * 16);
@@ -91,13 +105,22 @@ struct KVStager {
 
   // Loads the block starting at key0; only a block that reaches past L clamps its rows.
   __device__ __forceinline__ void load(const char* kbase, const char* vbase, size_t kstride,
-                                       size_t vstride, int key0, int L, int tid) {
+                                       size_t vstride, int key0, int L, int tid,
+                                       const float* rope = nullptr) {
     const bool tail = key0 + BK > L;
     {  // every thread loads (the spare ones re-read a chunk of the last row; only store() skips them)
       const char* p = kbase + (size_t)key0 * kstride + koff;
       if (tail) p += ((size_t)min(key0 + krow, L - 1) - (key0 + krow)) * kstride;
+      if constexpr (ROPE) {
+        const int j = tid % kKTpr;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) kr[i] = ld16(p + 16 * i);
+        for (int i = 0; i < KPT; ++i) kr[i] = ld16(p + 16 * kchunk(j, i));
+        // the table row of this thread's key (spare and unrotating threads read a valid one)
+        rope_load<E::kPerChunk>(rope, min(key0 + krow, L - 1), (j < H ? j : 0) * E::kPerChunk, cs);
+      } else {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) kr[i] = ld16(p + 16 * i);
+      }
     }
     if constexpr (Tile::kVRowMajor) {
       if (tid < kVActive) {
@@ -119,10 +142,18 @@ struct KVStager {
     }
   }
 
-  __device__ __forceinline__ void store(char* stage, int tid) const {
+  __device__ __forceinline__ void store(char* stage, int tid) {
     char* sk = stage;
     char* sv = stage + Tile::kKBytes;
-    if (tid < kKActive) {
+    if constexpr (ROPE) {
+      const int j = tid % kKTpr;
+      if (j < H) rope_rotate_chunk<E>(kr[0], kr[1], cs);
+      if (tid < kKActive) {
+        char* d = sk + (krow * Tile::kKStride) * E::kBytes;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) st16(d + 16 * kchunk(j, i), kr[i]);
+      }
+    } else if (tid < kKActive) {
       char* d = sk + (krow * Tile::kKStride) * E::kBytes + (tid % kKTpr) * KPT * 16;
 #pragma unroll
       for (int i = 0; i < KPT; ++i) st16(d + 16 * i, kr[i]);
@@ -229,7 +260,7 @@ constexpr float kLazyRescale = 8.f;  // log2 units
 #define MIMO_SETPRIO 0
 #endif
 
-template <typename E, int NW, int BK>
+template <typename E, int NW, int BK, bool ROPE>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   using Tile = PrefillTile<E, BK>;
   using Frag = typename E::Frag;
@@ -271,6 +302,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
     const char* qrow = (const char*)a.q + (((size_t)b * a.L + qload) * a.Hq + head) * kDQK * E::kBytes;
 #pragma unroll
     for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
+    if constexpr (ROPE) {
+      // fragments 0, 1 hold dims 16 kk + 8 half .. +7 of the rotated slice, 2, 3 their partners
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float cs[16];
+        rope_load<8>(a.rope, qload, 16 * kk + 8 * half, cs);
+        rope_rotate_frag<E>(qf[kk], qf[kk + 2], cs);
+      }
+    }
   }
 
   const float c = a.scale_log2;
@@ -285,16 +325,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   const int kstart = (K0 / BK) * BK;
   const int nblk = (P1 - kstart + BK - 1) / BK;
 
-  KVStager<E, NT, BK> st;
+  KVStager<E, NT, BK, ROPE> st;
   st.init(krow_stride, vrow_stride, tid);
-  st.load(kbase, vbase, krow_stride, vrow_stride, kstart, a.L, tid);
+  st.load(kbase, vbase, krow_stride, vrow_stride, kstart, a.L, tid, a.rope);
   st.store(smem, tid);
   wait_all();
   __syncthreads();
 
   for (int ib = 0; ib < nblk; ++ib) {
     const int key0 = kstart + ib * BK;
-    if (ib + 1 < nblk) st.load(kbase, vbase, krow_stride, vrow_stride, key0 + BK, a.L, tid);
+    if (ib + 1 < nblk) st.load(kbase, vbase, krow_stride, vrow_stride, key0 + BK, a.L, tid, a.rope);
 
     const bool skip = (key0 > p0 + kQT - 1) || (key0 + BK - 1 < p0 - a.window + 1) || (p0 >= a.L);
     if (!skip) {
@@ -377,7 +417,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
 
 // ---------------------------------------------------------------- sliding-window ring kernel
 
-template <int NB>
+template <int NB, bool ROPE>
 __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   using E = BF16;
   using Tile = PrefillTile<E, 32>;
@@ -427,13 +467,13 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
     __syncthreads();
   }
   {
-    KVStager<E, NT, 32> pro[NB];
+    KVStager<E, NT, 32, ROPE> pro[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) pro[j].init(krow_stride, vrow_stride, tid);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
       if (t0 - NB + 1 + j >= 0)
-        pro[j].load(kbase, vbase, krow_stride, vrow_stride, 32 * (t0 - NB + 1 + j), a.L, tid);
+        pro[j].load(kbase, vbase, krow_stride, vrow_stride, 32 * (t0 - NB + 1 + j), a.L, tid, a.rope);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
       if (t0 - NB + 1 + j >= 0) pro[j].store(smem + slot(t0 - NB + 1 + j) * Tile::kStageBytes, tid);
@@ -443,11 +483,12 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
     const char* qrow = qbase + (size_t)min(kQT * t0 + col, a.L - 1) * qrow_stride;
 #pragma unroll
     for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
+    // (with RoPE every tile's Q, this one included, is rotated inside its step)
   }
   wait_all();
   __syncthreads();
 
-  KVStager<E, NT, 32> st;
+  KVStager<E, NT, 32, ROPE> st;
   st.init(krow_stride, vrow_stride, tid);
   // one tile; the next tile's Q goes to the second register set, fetched before this tile's score
   // MFMAs (Q of tiles t0, t0 + 2, .. lives in qf, of t0 + 1, t0 + 3, .. in qg)
@@ -464,20 +505,37 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
     // the next tile's diagonal K/V block and Q stream in under this whole tile. The loads are
     // unconditional (on the last tile: this tile's block again, and one shared Q row, unused), so
     // that the compiler's wait counts see one straight-line sequence of loads and stores.
-    st.load(kbase, vbase, krow_stride, vrow_stride, 32 * min(t + 1, t1 - 1), a.L, tid);
+    st.load(kbase, vbase, krow_stride, vrow_stride, 32 * min(t + 1, t1 - 1), a.L, tid, a.rope);
     const char* qrow_next = has_next ? qbase + (size_t)min(p0 + kQT + col, a.L - 1) * qrow_stride : qbase;
 #pragma unroll
     for (int kk = 0; kk < kDQK / 16; ++kk) qn[kk] = global_q_frag<E>(qrow_next, kk, half);
+    // with RoPE, this tile's Q (loaded a tile ago) is rotated between the score MFMAs of the
+    // unrotated dims (kk >= 4) and those of the rotated ones, so the table read hides under them
+    float qcs[ROPE ? 2 : 1][16];
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) rope_load<8>(a.rope, qpos, 16 * kk + 8 * half, qcs[kk]);
+    }
     __builtin_amdgcn_sched_barrier(0);  // left alone, the scheduler sinks the Q loads below the MFMAs
 
     // scores of the whole window: block j holds keys 32 * (t - NB + 1 + j) ..
     f32x16 s[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) s[j] = zero16();
+    constexpr int kk0 = ROPE ? kRopeDims / 16 : 0;
 #pragma unroll
-    for (int kk = 0; kk < kDQK / 16; ++kk) {
+    for (int kk = kk0; kk < kDQK / 16; ++kk) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) s[j] = mma(lds_k_frag<E, 32>(smem + base[j], col, kk, half), qc[kk], s[j]);
+    }
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) rope_rotate_frag<E>(qc[kk], qc[kk + 2], qcs[kk]);
+#pragma unroll
+      for (int kk = 0; kk < kk0; ++kk) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) s[j] = mma(lds_k_frag<E, 32>(smem + base[j], col, kk, half), qc[kk], s[j]);
+      }
     }
 
     float rmax = -INFINITY;
@@ -548,7 +606,10 @@ template <typename E, int NW, int BK>
 static hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const long long n_wg = (long long)a.n_qblocks * a.B * a.Hkv * a.n_hchunks;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<E, NW, BK>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, a);
+  if (a.rope)
+    hipLaunchKernelGGL((prefill_kernel<E, NW, BK, true>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<E, NW, BK, false>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -573,7 +634,29 @@ static hipError_t launch_swa(PrefillArgs a, hipStream_t stream) {
   a.n_segments = (int)((n_tiles + per - 1) / per);
   const long long n_wg = units * a.n_segments;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_swa_kernel<NB>), dim3((unsigned)n_wg), dim3(512), 0, stream, a);
+  if (a.rope)
+    hipLaunchKernelGGL((prefill_swa_kernel<NB, true>), dim3((unsigned)n_wg), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_swa_kernel<NB, false>), dim3((unsigned)n_wg), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+// One thread per (position, pair): the angle and its cosine / sine in fp64, stored as fp32.
+__global__ __launch_bounds__(256) void rope_table_kernel(int n_pos, double base, float* table) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)n_pos * (kRopeDims / 2)) return;
+  const int p = (int)(idx / (kRopeDims / 2)), i = (int)(idx % (kRopeDims / 2));
+  const double ang = (double)p * pow(base, -2.0 * i / kRopeDims);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  reinterpret_cast<f32x2*>(table)[idx] = f32x2{(float)cs, (float)sn};
+}
+
+hipError_t rope_table_launch(int n_pos, double base, float* table, hipStream_t stream) {
+  const long long n = (long long)n_pos * (kRopeDims / 2);
+  const long long blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, n_pos, base, table);
   return hipGetLastError();
 }
 

@@ -37,6 +37,7 @@ class Workload:
     ring_offsets: bool = False
     seed: int = 0
     description: str = ""
+    rope_base: float = 0.0  # > 0: Q/K given before the rotary embedding (first 64 dims, this base)
 
     @property
     def elem(self) -> int:
@@ -76,6 +77,16 @@ WORKLOADS = {
         "ga_decode_mtp_bf16", "decode", "bf16", 64, 4, 1 << 30, B=64, T=4, C=16384, P=16384, seed=7,
         description="global decode bf16, 64 seqs x 16384 cached + 4 tokens, 64/4 heads, split-KV"),
 }
+
+# The same four bf16 workloads with Q/K given before the rotary embedding, rotated inside the
+# kernels (MiMo-V2-Flash Technical Report review (xllm-io), §3.1 and §4: first 64 dims, base 10K for
+# sliding-window layers, 5M for global layers). Same inputs (same seeds) as the plain workloads.
+for _name, _base in (("swa_prefill_bf16", 1e4), ("ga_prefill_bf16", 5e6), ("swa_decode_bf16", 1e4),
+                     ("ga_decode_bf16", 5e6)):
+    _w = WORKLOADS[_name]
+    _rn = _name.replace("_bf16", "_rope_bf16")
+    WORKLOADS[_rn] = Workload(**{**_w.__dict__, "name": _rn, "rope_base": _base,
+                                 "description": _w.description + f", RoPE base {_base:g} fused"})
 
 
 def prefill_scores(B: int, L: int, Hq: int, window: int) -> int:

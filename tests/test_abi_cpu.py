@@ -151,3 +151,56 @@ def test_binding_fails_loudly_without_gpu_tensors():
     x = torch.zeros(1, 4, 2, 192)
     with pytest.raises(ValueError):
         mimo.prefill(x, x[:, :, :1], torch.zeros(1, 4, 1, 128), window=4)
+
+
+# ------------------------------------------------------------------ rotary-embedding entry points
+
+@pytest.mark.parametrize("n_pos,rot,base,table,code", [
+    (0, 64, 1e4, P, EINVAL),
+    (100, 64, 1.0, P, EINVAL),
+    (100, 64, float("nan"), P, EINVAL),
+    (100, 64, float("inf"), P, EINVAL),
+    (100, 64, 1e4, None, EINVAL),
+    (100, 64, 1e4, P_MIS, EINVAL),
+    (100, 32, 1e4, P, EUNSUPPORTED),
+])
+def test_rope_table_validation(lib, n_pos, rot, base, table, code):
+    assert lib.mimo_attn_rope_table(n_pos, rot, base, table, None) == code
+    assert mimo.last_error() != ""
+
+
+def prefill_rope(lib, table=P, positions=64, rot=64, L=64, **kw):
+    a = dict(dt=BF16, B=1, Hq=64, Hkv=8, dqk=192, dv=128, q=P, k=P, v=P, window=128, sink=None,
+             kvm=None, scale=0.07, o=P, lse=None)
+    a.update(kw)
+    return lib.mimo_attn_prefill_rope(a["dt"], a["B"], L, a["Hq"], a["Hkv"], a["dqk"], a["dv"],
+                                      a["q"], a["k"], a["v"], a["window"], a["sink"], a["kvm"],
+                                      a["scale"], table, positions, rot, a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=None), EINVAL),
+    (dict(table=P_MIS), EINVAL),
+    (dict(positions=63), EINVAL),          # fewer table rows than positions
+    (dict(rot=128), EUNSUPPORTED),
+    (dict(B=0), EINVAL),                   # the plain prefill checks still apply
+    (dict(scale=0.0), EINVAL),
+])
+def test_prefill_rope_validation(lib, kw, code):
+    assert prefill_rope(lib, **kw) == code
+
+
+def decode_rope(lib, table=P, positions=1004, rot=64, max_len=1000, T=4):
+    return lib.mimo_attn_decode_rope(BF16, 4, T, 64, 8, 192, 128, P, P, P, P, P, 128, P, None, max_len,
+                                     128, None, None, 0.07, table, positions, rot, 0, None, 0,
+                                     P, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=None), EINVAL),
+    (dict(positions=1003), EINVAL),        # needs max_len + T rows
+    (dict(rot=0), EUNSUPPORTED),
+    (dict(T=5, positions=2000), EINVAL),   # the plain decode checks still apply
+])
+def test_decode_rope_validation(lib, kw, code):
+    assert decode_rope(lib, **kw) == code
