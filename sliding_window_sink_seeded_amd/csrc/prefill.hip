@@ -54,11 +54,14 @@ struct PrefillTile {
 // its 4-byte transposed writes hit distinct banks.
 // Rows at or past L are read from row L - 1 (finite data that the mask gives weight 0).
 //
-// ROPE: K arrives before the rotary embedding. Thread j < H of a K row (H = chunks per 32 dims)
+// ROPE (K arrives before the rotary embedding): thread j < H of a K row (H = chunks per 32 dims)
 // then holds the partner chunks j and j + H (dims 8j.. and 8j + 32.. for bf16) plus KPT - 2 chunks
-// of the unrotated dims, the other threads KPT chunks of the rest; load() also fetches the
-// (cos, sin) pairs of its key position and store() rotates the pair before writing LDS.
-template <typename E, int NT, int BK, bool ROPE = false>
+// of the unrotated dims, the other threads KPT chunks of the rest, and store() rotates the pair
+// before writing LDS, with the (cos, sin) of its key position fetched by load() from the table in
+// memory (kRopeMem) or read by store() from a [BK][32][2] table already in LDS (kRopeLds).
+constexpr int kRopeNone = 0, kRopeMem = 1, kRopeLds = 2;
+
+template <typename E, int NT, int BK, int ROPE = kRopeNone>
 struct KVStager {
   using Tile = PrefillTile<E, BK>;
   static constexpr int kKChunksRow = kDQK / E::kPerChunk;
@@ -66,7 +69,7 @@ struct KVStager {
   static_assert(kKChunksRow % KPT == 0, "a thread's K chunks stay in one row");
   static constexpr int kKTpr = kKChunksRow / KPT;  // threads per K row
   static constexpr int H = kRopeDims / 2 / E::kPerChunk;  // chunks in 32 dims
-  static_assert(!ROPE || (KPT >= 2 && kKTpr >= H), "each rotated chunk pair fits one thread");
+  static_assert(ROPE == kRopeNone || (KPT >= 2 && kKTpr >= H), "each rotated chunk pair fits one thread");
   // chunk (within the row) of this thread's i-th K chunk; j = thread index within the row
   __device__ static constexpr int kchunk(int j, int i) {
     if (!ROPE) return j * KPT + i;
@@ -85,7 +88,7 @@ struct KVStager {
   u32x4 vr[VPT];
   uint32_t koff, voff[Tile::kVRowMajor ? 1 : VPT];
   int krow, vrow;
-  float cs[ROPE ? 2 * E::kPerChunk : 1];  // (cos, sin) of this thread's rotated dims
+  float cs[ROPE == kRopeMem ? 2 * E::kPerChunk : 1];  // (cos, sin) of this thread's rotated dims
 
   __device__ __forceinline__ void init(size_t kstride, size_t vstride, int tid) {
     krow = min(tid / kKTpr, BK - 1);
@@ -111,12 +114,13 @@ struct KVStager {
     {  // every thread loads (the spare ones re-read a chunk of the last row; only store() skips them)
       const char* p = kbase + (size_t)key0 * kstride + koff;
       if (tail) p += ((size_t)min(key0 + krow, L - 1) - (key0 + krow)) * kstride;
-      if constexpr (ROPE) {
+      if constexpr (ROPE != kRopeNone) {
         const int j = tid % kKTpr;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) kr[i] = ld16(p + 16 * kchunk(j, i));
         // the table row of this thread's key (spare and unrotating threads read a valid one)
-        rope_load<E::kPerChunk>(rope, min(key0 + krow, L - 1), (j < H ? j : 0) * E::kPerChunk, cs);
+        if constexpr (ROPE == kRopeMem)
+          rope_load<E::kPerChunk>(rope, min(key0 + krow, L - 1), (j < H ? j : 0) * E::kPerChunk, cs);
       } else {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) kr[i] = ld16(p + 16 * i);
@@ -142,12 +146,25 @@ struct KVStager {
     }
   }
 
-  __device__ __forceinline__ void store(char* stage, int tid) {
+  __device__ __forceinline__ void store(char* stage, int tid, const char* lds_table = nullptr) {
     char* sk = stage;
     char* sv = stage + Tile::kKBytes;
-    if constexpr (ROPE) {
+    if constexpr (ROPE != kRopeNone) {
       const int j = tid % kKTpr;
-      if (j < H) rope_rotate_chunk<E>(kr[0], kr[1], cs);
+      if constexpr (ROPE == kRopeLds) {
+        if (j < H) {
+          float c[2 * E::kPerChunk];
+          const float* t = reinterpret_cast<const float*>(lds_table) + (krow * (kRopeDims / 2) + j * E::kPerChunk) * 2;
+#pragma unroll
+          for (int w = 0; w < E::kPerChunk / 2; ++w) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(t + 4 * w);
+            c[4 * w] = v[0]; c[4 * w + 1] = v[1]; c[4 * w + 2] = v[2]; c[4 * w + 3] = v[3];
+          }
+          rope_rotate_chunk<E>(kr[0], kr[1], c);
+        }
+      } else {
+        if (j < H) rope_rotate_chunk<E>(kr[0], kr[1], cs);
+      }
       if (tid < kKActive) {
         char* d = sk + (krow * Tile::kKStride) * E::kBytes;
 #pragma unroll
@@ -325,7 +342,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   const int kstart = (K0 / BK) * BK;
   const int nblk = (P1 - kstart + BK - 1) / BK;
 
-  KVStager<E, NT, BK, ROPE> st;
+  KVStager<E, NT, BK, ROPE ? kRopeMem : kRopeNone> st;
   st.init(krow_stride, vrow_stride, tid);
   st.load(kbase, vbase, krow_stride, vrow_stride, kstart, a.L, tid, a.rope);
   st.store(smem, tid);
@@ -422,7 +439,15 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   using E = BF16;
   using Tile = PrefillTile<E, 32>;
   constexpr int NW = 8, NT = 512, R = NB + 1;
-  __shared__ __attribute__((aligned(16))) char smem[R * Tile::kStageBytes];
+  // RoPE: three [32][32][2] fp32 (cos, sin) tables after the ring, for tiles t, t + 1, t + 2 (tile
+  // t's rows rotate its Q; tile t + 1's rows rotate the diagonal K block staged at the end of tile
+  // t; tile t + 2's rows are written at the end of tile t). The prologue's blocks are rotated in
+  // place in the ring.
+  constexpr int kHalfRot = kRopeDims / 2;
+  constexpr int kTblBytes = kQT * kHalfRot * 2 * 4;
+  __shared__ __attribute__((aligned(16))) char smem[R * Tile::kStageBytes + (ROPE ? 3 * kTblBytes : 0)];
+  char* tables = smem + R * Tile::kStageBytes;
+  auto table_of = [&](int tile) { return tables + (tile % 3) * kTblBytes; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -460,6 +485,26 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   // ring slot of key block kb (kb >= -NB + 1)
   auto slot = [](int kb) { return (kb + R) % R; };
 
+  // RoPE: rotate, in place, the rotated dims of the K rows of ring slot `sl`; thread tid takes
+  // row r = tid / 16 and the pairs (i, i + 32), (i + 1, i + 33) for i = 2 (tid % 16), with the
+  // (cos, sin) row `trow` of that key's position (in LDS or in memory)
+  auto rotate_block = [&](int sl, const float* trow) {
+    const int r = tid / (kHalfRot / 2), i = 2 * (tid % (kHalfRot / 2));
+    uint32_t* row = reinterpret_cast<uint32_t*>(smem + sl * Tile::kStageBytes + r * Tile::kKStride * 2);
+    const uint32_t lo = row[i / 2], hi = row[(i + kHalfRot) / 2];  // bf16 pairs (i, i+1), (i+32, i+33)
+    const f32x4 c = *reinterpret_cast<const f32x4*>(trow + i * 2);
+    const float x0 = __uint_as_float(lo << 16), x1 = __uint_as_float(lo & 0xFFFF0000u);
+    const float y0 = __uint_as_float(hi << 16), y1 = __uint_as_float(hi & 0xFFFF0000u);
+    row[i / 2] = pack_bf16x2(x0 * c[0] - y0 * c[1], x1 * c[2] - y1 * c[3]);
+    row[(i + kHalfRot) / 2] = pack_bf16x2(y0 * c[0] + x0 * c[1], y1 * c[2] + x1 * c[3]);
+  };
+  static_assert(NT == kQT * kHalfRot / 2, "one thread per two pairs of a 32-row block");
+  // this thread's 16 bytes of the (cos, sin) rows of positions p0 .. p0 + 31 (clamped into L)
+  auto table_chunk = [&](int p0) {
+    const int r = tid / 16, q4 = tid % 16;
+    return ld16(reinterpret_cast<const char*>(a.rope) + ((size_t)min(p0 + r, a.L - 1) * kHalfRot * 2 + 4 * q4) * 4);
+  };
+
   // prologue: zero the slots of blocks before position 0 (they are scored, masked, and must hold
   // finite values), then stage the window of tile t0 (blocks t0 - NB + 1 .. t0) and Q of tile t0
   if (t0 < NB - 1) {
@@ -467,16 +512,29 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
     __syncthreads();
   }
   {
-    KVStager<E, NT, 32, ROPE> pro[NB];
+    KVStager<E, NT, 32> pro[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) pro[j].init(krow_stride, vrow_stride, tid);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
       if (t0 - NB + 1 + j >= 0)
-        pro[j].load(kbase, vbase, krow_stride, vrow_stride, 32 * (t0 - NB + 1 + j), a.L, tid, a.rope);
+        pro[j].load(kbase, vbase, krow_stride, vrow_stride, 32 * (t0 - NB + 1 + j), a.L, tid);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
       if (t0 - NB + 1 + j >= 0) pro[j].store(smem + slot(t0 - NB + 1 + j) * Tile::kStageBytes, tid);
+    if constexpr (ROPE) {
+      // the window's blocks, rotated with table rows read from memory; rows of tiles t0 and
+      // t0 + 1 to LDS
+      st16(table_of(t0) + tid * 16, table_chunk(kQT * t0));
+      st16(table_of(t0 + 1) + tid * 16, table_chunk(kQT * min(t0 + 1, t1 - 1)));
+      wait_all();
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int kb = t0 - NB + 1 + j;
+        if (kb >= 0) rotate_block(slot(kb), a.rope + (size_t)min(32 * kb + tid / 16, a.L - 1) * kHalfRot * 2);
+      }
+    }
   }
   bf16x8 qf[kDQK / 16];
   {
@@ -488,7 +546,7 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   wait_all();
   __syncthreads();
 
-  KVStager<E, NT, 32, ROPE> st;
+  KVStager<E, NT, 32, ROPE ? kRopeLds : kRopeNone> st;
   st.init(krow_stride, vrow_stride, tid);
   // one tile; the next tile's Q goes to the second register set, fetched before this tile's score
   // MFMAs (Q of tiles t0, t0 + 2, .. lives in qf, of t0 + 1, t0 + 3, .. in qg)
@@ -505,37 +563,36 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
     // the next tile's diagonal K/V block and Q stream in under this whole tile. The loads are
     // unconditional (on the last tile: this tile's block again, and one shared Q row, unused), so
     // that the compiler's wait counts see one straight-line sequence of loads and stores.
-    st.load(kbase, vbase, krow_stride, vrow_stride, 32 * min(t + 1, t1 - 1), a.L, tid, a.rope);
+    st.load(kbase, vbase, krow_stride, vrow_stride, 32 * min(t + 1, t1 - 1), a.L, tid);
+    u32x4 tchunk;  // RoPE: this thread's share of the table rows of tile t + 2
+    if constexpr (ROPE) tchunk = table_chunk(kQT * min(t + 2, t1 - 1));
     const char* qrow_next = has_next ? qbase + (size_t)min(p0 + kQT + col, a.L - 1) * qrow_stride : qbase;
 #pragma unroll
     for (int kk = 0; kk < kDQK / 16; ++kk) qn[kk] = global_q_frag<E>(qrow_next, kk, half);
-    // with RoPE, this tile's Q (loaded a tile ago) is rotated between the score MFMAs of the
-    // unrotated dims (kk >= 4) and those of the rotated ones, so the table read hides under them
-    float qcs[ROPE ? 2 : 1][16];
-    if constexpr (ROPE) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) rope_load<8>(a.rope, qpos, 16 * kk + 8 * half, qcs[kk]);
-    }
     __builtin_amdgcn_sched_barrier(0);  // left alone, the scheduler sinks the Q loads below the MFMAs
+    if constexpr (ROPE) {
+      // this tile's Q (loaded a tile ago) rotated in registers with its rows' table in LDS
+      const float* trow = reinterpret_cast<const float*>(table_of(t)) + col * kHalfRot * 2;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float cs[16];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(trow + (16 * kk + 8 * half) * 2 + 4 * w);
+          cs[4 * w] = v[0]; cs[4 * w + 1] = v[1]; cs[4 * w + 2] = v[2]; cs[4 * w + 3] = v[3];
+        }
+        rope_rotate_frag<E>(qc[kk], qc[kk + 2], cs);
+      }
+    }
 
     // scores of the whole window: block j holds keys 32 * (t - NB + 1 + j) ..
     f32x16 s[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) s[j] = zero16();
-    constexpr int kk0 = ROPE ? kRopeDims / 16 : 0;
 #pragma unroll
-    for (int kk = kk0; kk < kDQK / 16; ++kk) {
+    for (int kk = 0; kk < kDQK / 16; ++kk) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) s[j] = mma(lds_k_frag<E, 32>(smem + base[j], col, kk, half), qc[kk], s[j]);
-    }
-    if constexpr (ROPE) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) rope_rotate_frag<E>(qc[kk], qc[kk + 2], qcs[kk]);
-#pragma unroll
-      for (int kk = 0; kk < kk0; ++kk) {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) s[j] = mma(lds_k_frag<E, 32>(smem + base[j], col, kk, half), qc[kk], s[j]);
-      }
     }
 
     float rmax = -INFINITY;
@@ -590,7 +647,10 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
     // tile's score MFMAs instead of holding up the loads that reuse their registers
     u32x4 out[8];
     pack_row_bf16(acc, 1.f / l, out);
-    if (has_next) st.store(smem + slot(t + 1) * Tile::kStageBytes, tid);
+    if (has_next) {
+      st.store(smem + slot(t + 1) * Tile::kStageBytes, tid, ROPE ? table_of(t + 1) : nullptr);
+      if constexpr (ROPE) st16(table_of(t + 2) + tid * 16, tchunk);
+    }
     store_packed_row_bf16(obase + (size_t)qpos * orow_stride, out, half);
     if (a.lse) a.lse[((size_t)b * a.Hq + head) * a.L + qpos] = (m + fast_log2(l)) * kLn2;
     __syncthreads();
