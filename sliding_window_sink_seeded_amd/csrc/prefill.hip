@@ -504,6 +504,20 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
     const int r = tid / 16, q4 = tid % 16;
     return ld16(reinterpret_cast<const char*>(a.rope) + ((size_t)min(p0 + r, a.L - 1) * kHalfRot * 2 + 4 * q4) * 4);
   };
+  // RoPE: rotate a tile's Q fragments in registers with that tile's table rows in LDS
+  auto rotate_q = [&](bf16x8(&q)[kDQK / 16], int tile) {
+    const float* trow = reinterpret_cast<const float*>(table_of(tile)) + col * kHalfRot * 2;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float cs[16];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(trow + (16 * kk + 8 * half) * 2 + 4 * w);
+        cs[4 * w] = v[0]; cs[4 * w + 1] = v[1]; cs[4 * w + 2] = v[2]; cs[4 * w + 3] = v[3];
+      }
+      rope_rotate_frag<E>(q[kk], q[kk + 2], cs);
+    }
+  };
 
   // prologue: zero the slots of blocks before position 0 (they are scored, masked, and must hold
   // finite values), then stage the window of tile t0 (blocks t0 - NB + 1 .. t0) and Q of tile t0
@@ -541,10 +555,10 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
     const char* qrow = qbase + (size_t)min(kQT * t0 + col, a.L - 1) * qrow_stride;
 #pragma unroll
     for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
-    // (with RoPE every tile's Q, this one included, is rotated inside its step)
   }
   wait_all();
   __syncthreads();
+  if constexpr (ROPE) rotate_q(qf, t0);  // later tiles' Q: at the end of the tile before
 
   KVStager<E, NT, 32, ROPE ? kRopeLds : kRopeNone> st;
   st.init(krow_stride, vrow_stride, tid);
@@ -570,20 +584,6 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int kk = 0; kk < kDQK / 16; ++kk) qn[kk] = global_q_frag<E>(qrow_next, kk, half);
     __builtin_amdgcn_sched_barrier(0);  // left alone, the scheduler sinks the Q loads below the MFMAs
-    if constexpr (ROPE) {
-      // this tile's Q (loaded a tile ago) rotated in registers with its rows' table in LDS
-      const float* trow = reinterpret_cast<const float*>(table_of(t)) + col * kHalfRot * 2;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        float cs[16];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(trow + (16 * kk + 8 * half) * 2 + 4 * w);
-          cs[4 * w] = v[0]; cs[4 * w + 1] = v[1]; cs[4 * w + 2] = v[2]; cs[4 * w + 3] = v[3];
-        }
-        rope_rotate_frag<E>(qc[kk], qc[kk + 2], cs);
-      }
-    }
 
     // scores of the whole window: block j holds keys 32 * (t - NB + 1 + j) ..
     f32x16 s[NB];
@@ -642,6 +642,11 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
         for (int db = 0; db < kDV / 32; ++db)
           acc[db] = mma(lds_vt_frag<E, 32>(smem + base[j] + Tile::kKBytes, db, ks, lane), pf[j][ks],
                         acc[db]);
+
+    // RoPE: the next tile's Q has arrived by now; rotate it here, off the next tile's path
+    if constexpr (ROPE) {
+      if (has_next) rotate_q(qn, t + 1);
+    }
 
     // ring update first, output stores last: the stores drain under the barrier and the next
     // tile's score MFMAs instead of holding up the loads that reuse their registers
