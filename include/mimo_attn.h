@@ -47,7 +47,7 @@ enum {
   MIMO_OK = 0,
   MIMO_EINVAL = -1,      /* a size, pointer, alignment, head map or window argument is invalid */
   MIMO_EUNSUPPORTED = -2, /* valid request that this build does not implement (dtype/dims)       */
-  MIMO_EWORKSPACE = -3,  /* decode workspace missing or smaller than the size query returned     */
+  MIMO_EWORKSPACE = -3,  /* workspace missing or smaller than the size query returned            */
   MIMO_EHIP = -4         /* the HIP runtime refused a launch                                      */
 };
 
@@ -156,6 +156,43 @@ int mimo_attn_decode_rope(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk
                           const float* rope_table, int rope_positions, int rot_dims,
                           int num_splits, void* workspace, size_t workspace_bytes, void* o,
                           float* lse, hipStream_t stream);
+
+/*
+ * Backward pass of mimo_attn_prefill: gradients of a scalar loss with respect to q, k, v and the
+ * sink, given the loss gradient d_o of the output (the sink is a learned per-head logit,
+ * MiMo-V2-Flash Technical Report review (xllm-io), §3.2; MiMo series notes (plmsmile),
+ * MiMo-V2-Flash > Learnable Attention Sink). With p_ij = exp(s_ij - lse_i) and D_i = <d_o_i, o_i>:
+ *
+ *     ds_ij = p_ij (<d_o_i, v_j> - D_i)
+ *     dq_i = scale sum_j ds_ij k_j       dk_j = scale sum_i ds_ij q_i       dv_j = sum_i p_ij d_o_i
+ *     dsink_h = -sum_{b,i} exp(sink_h - lse_i) D_i
+ *
+ * where dk, dv also sum over the query heads that share the KV head.
+ *
+ *   q, k, v, window, sink, kv_head_of_q, scale: exactly as passed to mimo_attn_prefill.
+ *   o   [B, L, Hq, d_v]  dtype dt, and lse [B, Hq, L] fp32: that call's outputs (lse required).
+ *   d_o [B, L, Hq, d_v]  dtype dt: gradient of the loss with respect to o.
+ *   dq  [B, L, Hq, d_qk], dk [B, L, Hkv, d_qk], dv [B, L, Hkv, d_v] dtype dt: written (overwritten,
+ *       not accumulated); they must not overlap the inputs.
+ *   dsink [Hq] fp32 device, nullable: written when non-NULL; must be NULL when sink is NULL.
+ *   workspace / workspace_bytes: device scratch of at least
+ *       mimo_attn_prefill_backward_workspace_size(B, L, Hq) bytes, 16-byte aligned; overwritten.
+ *
+ * Products run on bf16 operands for dt = MIMO_BF16 (p and ds are rounded to bf16 before their
+ * products, as the forward does with p) and accumulate in fp32; dt = MIMO_F32 stays in fp32.
+ * Errors: those of mimo_attn_prefill, plus MIMO_EINVAL for NULL or misaligned o, lse, d_o, dq,
+ * dk, dv, workspace or dsink, or a dsink without a sink; MIMO_EWORKSPACE when the workspace is
+ * too small.
+ */
+int mimo_attn_prefill_backward(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v,
+                               const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* d_o, int window, const float* sink,
+                               const int32_t* kv_head_of_q, float scale, void* dq, void* dk,
+                               void* dv, float* dsink, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Workspace bytes of mimo_attn_prefill_backward (0 for sizes < 1). */
+size_t mimo_attn_prefill_backward_workspace_size(int B, int L, int Hq);
 
 /* Thread-local description of the last non-zero return on this thread ("" if none). */
 const char* mimo_attn_last_error(void);

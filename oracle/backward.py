@@ -100,19 +100,22 @@ def prefill_backward(q, k, v, do, window, sink, scale, kv_head_of_q=None, block=
 
 
 def backward_rows(q, k, v, do, window, sink, scale, rows, kv_head_of_q=None):
-    """dq of selected query rows: rows = [(b, i)]; returns [n, Hq, dqk] (float64)."""
-    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    """dq of selected query rows: rows = [(b, i)]; returns [n, Hq, dqk] (float64).
+
+    Inputs may be any float arrays; only the slices a row needs are read (and widened).
+    """
     Hq = q.shape[2]
     kvm = default_kv_map(Hq, k.shape[2]) if kv_head_of_q is None else np.asarray(kv_head_of_q)
     out = np.empty((len(rows), Hq, q.shape[3]))
     for n, (b, i) in enumerate(rows):
         lo = max(0, i - window + 1)
+        qs, ks, vs, ds_ = (_f64(x[b, a:z]) for x, a, z in
+                           ((q, i, i + 1), (k, lo, i + 1), (v, lo, i + 1), (do, i, i + 1)))
         for h in range(Hq):
             g = kvm[h]
-            _, _, _, ds = _row_terms(q[b, i:i + 1, h], [i], k[b, lo:i + 1, g], np.arange(lo, i + 1),
-                                     v[b, lo:i + 1, g], do[b, i:i + 1, h], _sink_value(sink, h),
-                                     scale, window)
-            out[n, h] = scale * (ds @ k[b, lo:i + 1, g])[0]
+            _, _, _, ds = _row_terms(qs[:, h], [i], ks[:, g], np.arange(lo, i + 1), vs[:, g],
+                                     ds_[:, h], _sink_value(sink, h), scale, window)
+            out[n, h] = scale * (ds @ ks[:, g])[0]
     return out
 
 
@@ -120,23 +123,23 @@ def backward_keys(q, k, v, do, window, sink, scale, keys, kv_head_of_q=None):
     """dk and dv of selected key positions: keys = [(b, j)]; returns ([n, Hkv, dqk], [n, Hkv, dv]).
 
     Key j receives from query rows i in [j, min(L, j + W)); each such row's weights are computed
-    over that row's whole window.
+    over that row's whole window. Only the slices those rows need are read (and widened).
     """
-    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     L, Hq, Hkv = q.shape[1], q.shape[2], k.shape[2]
     kvm = default_kv_map(Hq, Hkv) if kv_head_of_q is None else np.asarray(kv_head_of_q)
     dk = np.zeros((len(keys), Hkv, k.shape[3]))
     dv = np.zeros((len(keys), Hkv, v.shape[3]))
     for n, (b, j) in enumerate(keys):
-        i1 = min(L, j + window)
-        i0 = j
+        i0, i1 = j, min(L, j + window)
         lo = max(0, i0 - window + 1)
         q_pos, k_pos = np.arange(i0, i1), np.arange(lo, i1)
+        qs, ks, vs, ds_ = (_f64(x[b, a:z]) for x, a, z in
+                           ((q, i0, i1), (k, lo, i1), (v, lo, i1), (do, i0, i1)))
         col = j - lo
         for h in range(Hq):
             g = kvm[h]
-            p, _, _, ds = _row_terms(q[b, i0:i1, h], q_pos, k[b, lo:i1, g], k_pos, v[b, lo:i1, g],
-                                     do[b, i0:i1, h], _sink_value(sink, h), scale, window)
-            dk[n, g] += scale * (ds[:, col] @ q[b, i0:i1, h])
-            dv[n, g] += p[:, col] @ do[b, i0:i1, h]
+            p, _, _, ds = _row_terms(qs[:, h], q_pos, ks[:, g], k_pos, vs[:, g], ds_[:, h],
+                                     _sink_value(sink, h), scale, window)
+            dk[n, g] += scale * (ds[:, col] @ qs[:, h])
+            dv[n, g] += p[:, col] @ ds_[:, h]
     return dk, dv

@@ -9,6 +9,7 @@ fallback. If the shared library is missing, every call raises.
     o, lse = decode(q, k_new, v_new, k_cache, v_cache, cache_len, window=128, ...)
     table = rope_table(n_pos, base=1e4)                        # RoPE (cos, sin), device fp32
     o, lse = prefill(q, k, v, 128, sink=sink, rope=table)      # q, k given before RoPE
+    dq, dk, dv, dsink = prefill_backward(q, k, v, o, lse, do, 128, sink=sink)
 """
 
 from __future__ import annotations
@@ -17,12 +18,14 @@ import ctypes
 import math
 import os
 
-__all__ = ["prefill", "decode", "decode_workspace_size", "rope_table", "last_error", "version",
-           "library", "LIB_PATH", "MimoError", "EXPORTS", "ROPE_DIMS"]
+__all__ = ["prefill", "decode", "decode_workspace_size", "rope_table", "prefill_backward",
+           "backward_workspace_size", "last_error", "version", "library", "LIB_PATH", "MimoError",
+           "EXPORTS", "ROPE_DIMS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmimo_attn.so")
 EXPORTS = ("mimo_attn_prefill", "mimo_attn_decode", "mimo_attn_decode_workspace_size",
            "mimo_attn_rope_table", "mimo_attn_prefill_rope", "mimo_attn_decode_rope",
+           "mimo_attn_prefill_backward", "mimo_attn_prefill_backward_workspace_size",
            "mimo_attn_last_error", "mimo_attn_version")
 ROPE_DIMS = 64  # rotated leading Q/K dims
 
@@ -65,6 +68,12 @@ def library() -> ctypes.CDLL:
                                           i32, vp, vp, i32, i32, vp, vp, f32, vp, i32, i32, i32, vp,
                                           sz, vp, vp, vp]
     lib.mimo_attn_decode_rope.restype = i32
+    lib.mimo_attn_prefill_backward.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                                vp, vp, i32, vp, vp, f32, vp, vp, vp, vp, vp, sz,
+                                                vp]
+    lib.mimo_attn_prefill_backward.restype = i32
+    lib.mimo_attn_prefill_backward_workspace_size.argtypes = [i32, i32, i32]
+    lib.mimo_attn_prefill_backward_workspace_size.restype = sz
     lib.mimo_attn_last_error.argtypes = []
     lib.mimo_attn_last_error.restype = ctypes.c_char_p
     lib.mimo_attn_version.argtypes = []
@@ -266,3 +275,59 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_len, window: int, max_cache_
     del keep
     _check(rc)
     return out, lse
+
+
+def backward_workspace_size(B: int, L: int, Hq: int) -> int:
+    return int(library().mimo_attn_prefill_backward_workspace_size(B, L, Hq))
+
+
+def prefill_backward(q, k, v, o, lse, d_o, window: int, sink=None, scale: float | None = None,
+                     kv_map=None, want_dsink: bool = True, workspace=None, out=None, stream=None):
+    """Gradients of a prefill: returns (dq, dk, dv, dsink or None).
+
+    q, k, v, window, sink, scale, kv_map as passed to prefill(); o and lse are its outputs (lse
+    [B, Hq, L] fp32 is required); d_o [B, L, Hq, dv] is the loss gradient of o. out: optional
+    (dq, dk, dv) tensors to write. dsink [Hq] fp32 is returned when there is a sink and want_dsink.
+    """
+    import torch
+
+    _dev(q, "q", ndim=4)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("o", o), ("d_o", d_o)):
+        _dev(t, name, q.dtype, 4)
+    B, L, Hq, dqk = q.shape
+    Hkv, dv_ = k.shape[2], v.shape[3]
+    if (tuple(k.shape) != (B, L, Hkv, dqk) or tuple(v.shape) != (B, L, Hkv, dv_)
+            or tuple(o.shape) != (B, L, Hq, dv_) or tuple(d_o.shape) != (B, L, Hq, dv_)):
+        raise ValueError("q, k, v, o, d_o shapes disagree")
+    _dev(lse, "lse", torch.float32, 3)
+    if tuple(lse.shape) != (B, Hq, L):
+        raise ValueError("lse has the wrong shape")
+    if sink is not None:
+        _dev(sink, "sink", torch.float32, 1)
+        if sink.shape[0] != Hq:
+            raise ValueError("sink must have Hq entries")
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _dev(t, name, q.dtype, 4)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} has the wrong shape")
+    dsink = None
+    if sink is not None and want_dsink:
+        dsink = torch.empty(Hq, dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    ws_bytes = backward_workspace_size(B, L, Hq)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_have = workspace.numel() * workspace.element_size()
+    keep, kvm = _kv_map(kv_map, Hq)
+    rc = library().mimo_attn_prefill_backward(dt, B, L, Hq, Hkv, dqk, dv_, _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(o), _ptr(lse), _ptr(d_o), int(window), _ptr(sink),
+                                              kvm, float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                              _ptr(dsink), _ptr(workspace), ws_have, _stream(stream))
+    del keep
+    _check(rc)
+    return dq, dk, dv, dsink

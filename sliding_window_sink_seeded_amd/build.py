@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmimo_attn.so")
-SOURCES = ["api.hip", "prefill.hip", "decode.hip"]
+SOURCES = ["api.hip", "prefill.hip", "decode.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -134,6 +134,54 @@ int mimo_attn_prefill_rope(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_q
                       rope_table, o, lse, stream);
 }
 
+size_t mimo_attn_prefill_backward_workspace_size(int B, int L, int Hq) {
+  if (B < 1 || L < 1 || Hq < 1) return 0;
+  return mimo::backward_ws_bytes(B, L, Hq);
+}
+
+int mimo_attn_prefill_backward(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v,
+                               const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* d_o, int window, const float* sink,
+                               const int32_t* kv_head_of_q, float scale, void* dq, void* dk,
+                               void* dv, float* dsink, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  g_err.clear();
+  if (int rc = check_common(dt, B, Hq, Hkv, d_qk, d_v, window, scale)) return rc;
+  if (L < 1) return fail(MIMO_EINVAL, "L must be >= 1");
+  if (L > (1 << 30)) return fail(MIMO_EUNSUPPORTED, "L %d exceeds 2^30", L);
+  if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv)
+    return fail(MIMO_EINVAL, "q, k, v, o, lse, d_o, dq, dk and dv must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(MIMO_EINVAL, "q, k, v, o, d_o, dq, dk and dv must be 16-byte aligned");
+  if (!aligned4(lse) || (sink && !aligned4(sink)) || (dsink && !aligned4(dsink)))
+    return fail(MIMO_EINVAL, "lse, sink and dsink must be 4-byte aligned");
+  if (dsink && !sink) return fail(MIMO_EINVAL, "dsink given without a sink");
+  const double elem = dt == MIMO_BF16 ? 2.0 : 4.0;
+  if ((double)B * L * Hq * d_qk * elem > 4.6e18) return fail(MIMO_EINVAL, "tensor too large");
+  const size_t need = mimo::backward_ws_bytes(B, L, Hq);
+  if (!workspace || !aligned16(workspace))
+    return fail(MIMO_EINVAL, "workspace must be non-NULL and 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(MIMO_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+
+  mimo::BackwardArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.d_o = d_o; a.lse = lse; a.sink = sink;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dsink = dsink;
+  a.D = static_cast<float*>(workspace);
+  a.sink_part = dsink ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                 mimo::backward_ws_d_bytes(B, L, Hq))
+                      : nullptr;
+  a.B = B; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.window = window < L ? window : L;
+  a.scale = scale;
+  a.scale_log2 = scale * mimo::kLog2e;
+  if (int rc = group_heads(Hq, Hkv, kv_head_of_q, &a.hl)) return rc;
+  const hipError_t e = mimo::backward_launch(dt == MIMO_BF16, a, stream);
+  if (e != hipSuccess) return fail(MIMO_EHIP, "backward launch failed: %s", hipGetErrorString(e));
+  return MIMO_OK;
+}
+
 int mimo_attn_rope_table(int n_pos, int rot_dims, double base, float* table, hipStream_t stream) {
   g_err.clear();
   if (rot_dims != mimo::kRopeDims)

@@ -1,0 +1,409 @@
+// Backward kernels: gradients of sink-seeded sliding-window / causal attention on gfx950 MFMA.
+//
+// Operation: the gradient of the prefill (MiMo-V2-Flash Technical Report review (xllm-io), §3.1
+// and §3.2; MiMo series notes (plmsmile), MiMo-V2-Flash > Learnable Attention Sink: the sink is a
+// learned per-head logit in the softmax denominator with no value vector, so training also needs
+// its gradient). With the forward's lse (sink included), for query row i and visible key j:
+//   P_ij = exp(s_ij - lse_i),  D_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, v_j> - D_i)
+//   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i
+//   d s_h = -sum_i exp(s_h - lse_i) D_i
+// (dK and dV also sum over the query heads of the KV head, and d s_h over the batch).
+//
+// Three kernels on the caller's stream, no atomics (every output element has one writer, so the
+// results do not depend on scheduling):
+// bwd_dq_kernel (query-major, the forward's streaming structure): a wave owns one query head and
+//   32 query rows (one per MFMA column). It forms D for its rows from dO and O, writes it to the
+//   workspace together with its rows' share of the sink gradient, then streams the K/V blocks of
+//   the window through LDS: S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+// bwd_dkdv_kernel (key-major): a wave owns 32 keys, one per MFMA column, whose K and V rows stay
+//   in registers as MFMA operands. The workgroup walks (query head of the group, 32-row query tile)
+//   steps; each step's Q, dO, lse and D rows are staged through LDS (double-buffered) and shared by
+//   every wave: S = Q K^T, P, dP = dO V^T, dS; dV^T += dO^T P and dK^T += Q^T dS take P and dS
+//   straight from the accumulators.
+// bwd_sink_kernel: sums the per-tile sink partials of each head in a fixed order.
+#include "tiles.hpp"
+
+namespace mimo {
+
+template <typename E>
+__device__ __forceinline__ void frag_to_f32(const typename E::Frag& f, float (&x)[8]) {
+  if constexpr (E::kBytes == 2) {
+    const u32x4 u = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      x[2 * w] = __uint_as_float(u[w] << 16);
+      x[2 * w + 1] = __uint_as_float(u[w] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = f[e];
+  }
+}
+
+// ------------------------------------------------------------------------------------- dQ kernel
+
+template <typename E, int NW, int BK>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
+  using Tile = PrefillTile<E, BK, kVRows>;
+  using Frag = typename E::Frag;
+  constexpr int NT = NW * 64;
+  constexpr int NSB = BK / 32;
+  __shared__ __attribute__((aligned(16))) char smem[2 * Tile::kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // heaviest query blocks (latest positions) first
+  const int per_q = a.B * a.Hkv * a.n_hchunks;
+  const int qb = a.n_qblocks - 1 - (int)(blockIdx.x / per_q);
+  int rest = blockIdx.x % per_q;
+  const int hc = rest % a.n_hchunks;
+  rest /= a.n_hchunks;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+
+  const int HG = a.heads_per_wg;
+  const int qtiles = NW / HG;
+  const int head = a.hl.at(g * a.G + hc * HG + wave % HG);
+  const int P0 = qb * kQT * qtiles;
+  const int P1 = min(a.L, P0 + kQT * qtiles);
+  const int p0 = P0 + kQT * (wave / HG);
+  const int qpos = p0 + col;
+  const bool valid = qpos < a.L;
+  const int qload = min(qpos, a.L - 1);
+
+  const size_t krow_stride = (size_t)a.Hkv * kDQK * E::kBytes;
+  const size_t vrow_stride = (size_t)a.Hkv * kDV * E::kBytes;
+  const char* kbase = (const char*)a.k + ((size_t)b * a.L * a.Hkv + g) * kDQK * E::kBytes;
+  const char* vbase = (const char*)a.v + ((size_t)b * a.L * a.Hkv + g) * kDV * E::kBytes;
+
+  // Q fragments (B operand of S^T = K Q^T) and dO fragments (B operand of dP^T = V dO^T)
+  const size_t row = ((size_t)b * a.L + qload) * a.Hq + head;
+  Frag qf[kDQK / 16], df[kDV / 16];
+  {
+    const char* qrow = (const char*)a.q + row * kDQK * E::kBytes;
+    const char* drow = (const char*)a.d_o + row * kDV * E::kBytes;
+#pragma unroll
+    for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
+#pragma unroll
+    for (int kk = 0; kk < kDV / 16; ++kk) df[kk] = global_q_frag<E>(drow, kk, half);
+  }
+  // D = <dO, O> of this row; each wave half holds 64 of the 128 elements
+  float D;
+  {
+    const char* orow = (const char*)a.o + row * kDV * E::kBytes;
+    float part = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < kDV / 16; ++kk) {
+      float x[8], y[8];
+      frag_to_f32<E>(df[kk], x);
+      frag_to_f32<E>(global_q_frag<E>(orow, kk, half), y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = __builtin_fmaf(x[e], y[e], part);
+    }
+    D = halves_sum(part);
+  }
+  const size_t lrow = ((size_t)b * a.Hq + head) * a.L + qload;
+  const float lse2 = a.lse[lrow] * kLog2e;
+  if (half == 0 && valid) a.D[lrow] = D;
+  if (a.sink_part && p0 < a.L) {
+    // this tile's share of d s_h: -sum_i exp(s_h - lse_i) D_i (the sign is applied at the end)
+    float t = (half == 0 && valid) ? fast_exp2(a.sink[head] * kLog2e - lse2) * D : 0.f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+    if (lane == 0) a.sink_part[((size_t)head * a.B + b) * a.n_qtiles + p0 / kQT] = t;
+  }
+
+  const float c = a.scale_log2;
+  f32x16 acc[kDQK / 32];
+#pragma unroll
+  for (int t = 0; t < kDQK / 32; ++t) acc[t] = zero16();
+
+  const int K0 = max(0, P0 - a.window + 1);
+  const int kstart = (K0 / BK) * BK;
+  const int nblk = (P1 - kstart + BK - 1) / BK;
+
+  KVStager<E, NT, BK, kRopeNone, kVRows> st;
+  st.init(krow_stride, vrow_stride, tid);
+  st.load(kbase, vbase, krow_stride, vrow_stride, kstart, a.L, tid);
+  st.store(smem, tid);
+  wait_all();
+  __syncthreads();
+
+  for (int ib = 0; ib < nblk; ++ib) {
+    const int key0 = kstart + ib * BK;
+    if (ib + 1 < nblk) st.load(kbase, vbase, krow_stride, vrow_stride, key0 + BK, a.L, tid);
+
+    const bool skip = (key0 > p0 + kQT - 1) || (key0 + BK - 1 < p0 - a.window + 1) || (p0 >= a.L);
+    if (!skip) {
+      const char* sk = smem + (ib & 1) * Tile::kStageBytes;
+      const char* sv = sk + Tile::kKBytes;
+      const bool need_mask = !((key0 + BK - 1 <= p0) && (p0 + kQT - 1 - key0 < a.window));
+
+      f32x16 s[NSB], dp[NSB];
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) s[sb] = dp[sb] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < kDQK / 16; ++kk)
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
+          s[sb] = mma(lds_row_frag<E>(sk, Tile::kKStride, 32 * sb + col, kk, half), qf[kk], s[sb]);
+#pragma unroll
+      for (int kk = 0; kk < kDV / 16; ++kk)
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
+          dp[sb] = mma(lds_row_frag<E>(sv, Tile::kVStride, 32 * sb + col, kk, half), df[kk], dp[sb]);
+
+      // dS^T = P^T (dP^T - D), P^T = exp(S^T * scale - lse), zero where masked
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[sb][r], c, -lse2));
+          if (need_mask) {
+            const int key = key0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int d = qpos - key;
+            p = (d >= 0 && d < a.window) ? p : 0.f;
+          }
+          s[sb][r] = p * (dp[sb][r] - D);
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const Frag dsf = frag_from_acc<E>(s[ks >> 1], 8 * (ks & 1));
+#pragma unroll
+        for (int t = 0; t < kDQK / 32; ++t)
+          acc[t] = mma(lds_t_frag<E>(sk, Tile::kKStride, t, ks, lane), dsf, acc[t]);
+      }
+    }
+
+    if (ib + 1 < nblk) st.store(smem + ((ib + 1) & 1) * Tile::kStageBytes, tid);
+    __syncthreads();
+  }
+
+  char* dqrow = (char*)a.dq + row * kDQK * E::kBytes;
+  store_out_row<E>(dqrow, acc, a.scale, half, valid);
+}
+
+// ---------------------------------------------------------------------------------- dK/dV kernel
+
+// LDS stage of one step: Q rows [32][kQS], dO rows [32][kOS], then lse * log2(e) [32] and D [32].
+// Row strides are padded so that both the 16-byte row reads and the transposing reads of the MFMA
+// operands spread over the banks.
+template <typename E>
+struct DkdvStage {
+  static constexpr int kQS = kDQK + 16 / E::kBytes;
+  static constexpr int kOS = E::kBytes == 2 ? kDV + 24 : kDV + 4;
+  static constexpr int kQBytes = kQT * kQS * E::kBytes;
+  static constexpr int kOBytes = kQT * kOS * E::kBytes;
+  static constexpr int kBytes = kQBytes + kOBytes + 2 * kQT * 4;
+  static_assert(kQBytes % 16 == 0 && kOBytes % 16 == 0, "16-byte aligned rows");
+};
+
+template <typename E, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a) {
+  using Frag = typename E::Frag;
+  using St = DkdvStage<E>;
+  constexpr int NT = NW * 64;
+  static_assert(NT == 256, "staging assumes 8 threads per staged row");
+  constexpr int QPT = kDQK * E::kBytes / 16 / 8;  // 16-byte Q chunks per thread
+  constexpr int OPT = kDV * E::kBytes / 16 / 8;   // 16-byte dO chunks per thread
+  __shared__ __attribute__((aligned(16))) char smem[2 * St::kBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // key blocks in ascending order: under causal attention the first ones see the most queries
+  const int kb = (int)(blockIdx.x / (a.B * a.Hkv));
+  const int rest = blockIdx.x % (a.B * a.Hkv);
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  const int kb0 = kb * 32 * NW;
+  const int kw0 = kb0 + 32 * wave;  // this wave's first key
+  const int kpos = kw0 + col;       // this lane's key
+  const int kload = min(kpos, a.L - 1);
+
+  // K and V rows of this lane's key as MFMA B operands (lane = key column)
+  const size_t krow = ((size_t)b * a.L + kload) * a.Hkv + g;
+  Frag kf[kDQK / 16], vf[kDV / 16];
+  {
+    const char* kr = (const char*)a.k + krow * kDQK * E::kBytes;
+    const char* vr = (const char*)a.v + krow * kDV * E::kBytes;
+#pragma unroll
+    for (int kk = 0; kk < kDQK / 16; ++kk) kf[kk] = global_q_frag<E>(kr, kk, half);
+#pragma unroll
+    for (int kk = 0; kk < kDV / 16; ++kk) vf[kk] = global_q_frag<E>(vr, kk, half);
+  }
+
+  // query tiles that see any key of the block
+  const int last_q = min(a.L - 1, kb0 + 32 * NW - 1 + a.window - 1);
+  const int qt0 = kb0 / kQT;
+  const int ntiles = last_q / kQT - qt0 + 1;
+  const int nsteps = a.G * ntiles;
+
+  // staging: thread tid moves row tid / 8 of the step's Q and dO tiles; threads 0..63 also move
+  // lse (rows 0..31) and D (rows 32..63 -> D of row tid - 32)
+  const int srow = tid >> 3, spart = tid & 7;
+  const size_t qrow_stride = (size_t)a.Hq * kDQK * E::kBytes;
+  const size_t orow_stride = (size_t)a.Hq * kDV * E::kBytes;
+  u32x4 qr[QPT], orr[OPT];
+  float lr = 0.f;
+  auto load_step = [&](int step) {
+    const int j = step / ntiles;
+    const int q0 = (qt0 + step % ntiles) * kQT;
+    const int head = a.hl.at(g * a.G + j);
+    const int qrow = min(q0 + srow, a.L - 1);
+    const char* qp = (const char*)a.q + ((size_t)b * a.L + qrow) * qrow_stride + (size_t)head * kDQK * E::kBytes;
+    const char* op = (const char*)a.d_o + ((size_t)b * a.L + qrow) * orow_stride + (size_t)head * kDV * E::kBytes;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) qr[i] = ld16(qp + 16 * (spart * QPT + i));
+#pragma unroll
+    for (int i = 0; i < OPT; ++i) orr[i] = ld16(op + 16 * (spart * OPT + i));
+    if (tid < 2 * kQT) {
+      const int r = min(q0 + (tid & 31), a.L - 1);
+      const size_t li = ((size_t)b * a.Hq + head) * a.L + r;
+      lr = tid < kQT ? a.lse[li] * kLog2e : a.D[li];
+    }
+  };
+  auto store_step = [&](char* stage) {
+    char* sq = stage + (srow * St::kQS + spart * QPT * (16 / E::kBytes)) * E::kBytes;
+    char* so = stage + St::kQBytes + (srow * St::kOS + spart * OPT * (16 / E::kBytes)) * E::kBytes;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) st16(sq + 16 * i, qr[i]);
+#pragma unroll
+    for (int i = 0; i < OPT; ++i) st16(so + 16 * i, orr[i]);
+    if (tid < 2 * kQT) reinterpret_cast<float*>(stage + St::kQBytes + St::kOBytes)[tid] = lr;
+  };
+
+  f32x16 acck[kDQK / 32], accv[kDV / 32];
+#pragma unroll
+  for (int t = 0; t < kDQK / 32; ++t) acck[t] = zero16();
+#pragma unroll
+  for (int t = 0; t < kDV / 32; ++t) accv[t] = zero16();
+
+  const float c = a.scale_log2;
+  load_step(0);
+  store_step(smem);
+  wait_all();
+  __syncthreads();
+
+  for (int step = 0; step < nsteps; ++step) {
+    if (step + 1 < nsteps) load_step(step + 1);
+    const int q0 = (qt0 + step % ntiles) * kQT;
+    const bool skip = (kw0 >= a.L) || (q0 + kQT - 1 < kw0) || (q0 > kw0 + 31 + a.window - 1);
+    if (!skip) {
+      const char* stage = smem + (step & 1) * St::kBytes;
+      const char* sq = stage;
+      const char* so = stage + St::kQBytes;
+      const float* sl = reinterpret_cast<const float*>(stage + St::kQBytes + St::kOBytes);
+      const bool need_mask =
+          !((q0 >= kw0 + 31) && (q0 + kQT - 1 - kw0 < a.window) && (q0 + kQT - 1 < a.L));
+
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int kk = 0; kk < kDQK / 16; ++kk) s = mma(lds_row_frag<E>(sq, St::kQS, col, kk, half), kf[kk], s);
+#pragma unroll
+      for (int kk = 0; kk < kDV / 16; ++kk) dp = mma(lds_row_frag<E>(so, St::kOS, col, kk, half), vf[kk], dp);
+
+      // register r holds query row 8 (r / 4) + 4 half + r % 4 of the tile
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 8 * gq + 4 * half);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + kQT + 8 * gq + 4 * half);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * gq + i;
+          float p = fast_exp2(__builtin_fmaf(s[r], c, -l4[i]));
+          if (need_mask) {
+            const int qp = q0 + 8 * gq + 4 * half + i;
+            const int d = qp - kpos;
+            p = (d >= 0 && d < a.window && qp < a.L) ? p : 0.f;
+          }
+          s[r] = p;
+          dp[r] = p * (dp[r] - d4[i]);
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < kQT / 16; ++ks) {
+        const Frag pf = frag_from_acc<E>(s, 8 * ks);
+#pragma unroll
+        for (int t = 0; t < kDV / 32; ++t) accv[t] = mma(lds_t_frag<E>(so, St::kOS, t, ks, lane), pf, accv[t]);
+        const Frag dsf = frag_from_acc<E>(dp, 8 * ks);
+#pragma unroll
+        for (int t = 0; t < kDQK / 32; ++t) acck[t] = mma(lds_t_frag<E>(sq, St::kQS, t, ks, lane), dsf, acck[t]);
+      }
+    }
+    if (step + 1 < nsteps) store_step(smem + ((step + 1) & 1) * St::kBytes);
+    __syncthreads();
+  }
+
+  const bool kvalid = kpos < a.L;
+  char* dkrow = (char*)a.dk + krow * kDQK * E::kBytes;
+  char* dvrow = (char*)a.dv + krow * kDV * E::kBytes;
+  store_out_row<E>(dkrow, acck, a.scale, half, kvalid);
+  store_out_row<E>(dvrow, accv, 1.f, half, kvalid);
+}
+
+// ---------------------------------------------------------------------------- sink gradient
+
+__global__ __launch_bounds__(256) void bwd_sink_kernel(const BackwardArgs a) {
+  __shared__ float red[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int n = a.B * a.n_qtiles;
+  const float* p = a.sink_part + (size_t)h * n;
+  float t = 0.f;
+  for (int i = tid; i < n; i += 256) t += p[i];
+  red[tid] = t;
+  __syncthreads();
+#pragma unroll
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) a.dsink[h] = -red[0];
+}
+
+// ------------------------------------------------------------------------------------ launchers
+
+size_t backward_ws_d_bytes(int B, int L, int Hq) {
+  const size_t d = (size_t)B * Hq * L * 4;
+  return (d + 255) / 256 * 256;
+}
+
+size_t backward_ws_bytes(int B, int L, int Hq) {
+  const size_t n_qtiles = ((size_t)L + kQT - 1) / kQT;
+  return backward_ws_d_bytes(B, L, Hq) + (size_t)Hq * B * n_qtiles * 4;
+}
+
+template <typename E>
+static hipError_t launch_backward(BackwardArgs a, hipStream_t stream) {
+  constexpr int NW = 8, BK = 32, NWK = 4;
+  int hg = 1;
+  while (hg < NW && a.G % (hg * 2) == 0) hg *= 2;
+  a.heads_per_wg = hg;
+  a.n_hchunks = a.G / hg;
+  const int rows_per_wg = kQT * (NW / hg);
+  a.n_qblocks = (a.L + rows_per_wg - 1) / rows_per_wg;
+  a.n_kblocks = (a.L + 32 * NWK - 1) / (32 * NWK);
+  a.n_qtiles = (a.L + kQT - 1) / kQT;
+
+  const long long n_dq = (long long)a.n_qblocks * a.B * a.Hkv * a.n_hchunks;
+  const long long n_kv = (long long)a.n_kblocks * a.B * a.Hkv;
+  if (n_dq > 0x7fffffffLL || n_kv > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((bwd_dq_kernel<E, NW, BK>), dim3((unsigned)n_dq), dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, NWK>), dim3((unsigned)n_kv), dim3(NWK * 64), 0, stream, a);
+  if (a.dsink) hipLaunchKernelGGL(bwd_sink_kernel, dim3(a.Hq), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t backward_launch(bool bf16, BackwardArgs a, hipStream_t stream) {
+  return bf16 ? launch_backward<BF16>(a, stream) : launch_backward<F32>(a, stream);
+}
+
+}  // namespace mimo

@@ -137,13 +137,15 @@ __device__ __forceinline__ u32x4 zero_chunk() {
   return z;
 }
 
-// Packs this lane's query column of a 32 x 128 O^T accumulator block into bf16 output chunks.
-// acc[db][r] holds O[col][32 db + 8 (r / 4) + 4 half + r % 4]. The two wave halves trade register
-// groups so that every lane owns 8 consecutive outputs: chunk i = 2 db + j covers outputs
-// 32 db + 16 j + 8 half .. +7. Every lane must call it (the exchange reads the partner lane).
-__device__ __forceinline__ void pack_row_bf16(const f32x16 (&acc)[4], float inv, u32x4 (&out)[8]) {
+// Packs this lane's column of a 32 x (32 N) transposed accumulator block into bf16 chunks.
+// acc[db][r] holds element 32 db + 8 (r / 4) + 4 half + r % 4 of the lane's row. The two wave
+// halves trade register groups so that every lane owns 8 consecutive outputs: chunk i = 2 db + j
+// covers outputs 32 db + 16 j + 8 half .. +7. Every lane must call it (the exchange reads the
+// partner lane).
+template <int N>
+__device__ __forceinline__ void pack_row_bf16(const f32x16 (&acc)[N], float inv, u32x4 (&out)[2 * N]) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < N; ++db) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int g0 = 8 * j, g1 = 8 * j + 4;  // register offsets of groups 2j and 2j+1
@@ -160,14 +162,16 @@ __device__ __forceinline__ void pack_row_bf16(const f32x16 (&acc)[4], float inv,
     }
   }
 }
-__device__ __forceinline__ void store_packed_row_bf16(char* orow, const u32x4 (&out)[8], int half) {
+template <int M>
+__device__ __forceinline__ void store_packed_row_bf16(char* orow, const u32x4 (&out)[M], int half) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(orow + (16 * i + 8 * half) * 2) = out[i];
+  for (int i = 0; i < M; ++i) *reinterpret_cast<u32x4*>(orow + (16 * i + 8 * half) * 2) = out[i];
 }
 // pack + store; lanes with !store write nothing but still take part in the exchange
-__device__ __forceinline__ void store_row_bf16(char* orow, const f32x16 (&acc)[4], float inv,
+template <int N>
+__device__ __forceinline__ void store_row_bf16(char* orow, const f32x16 (&acc)[N], float inv,
                                                int half, bool store) {
-  u32x4 out[8];
+  u32x4 out[2 * N];
   pack_row_bf16(acc, inv, out);
   if (store) store_packed_row_bf16(orow, out, half);
 }

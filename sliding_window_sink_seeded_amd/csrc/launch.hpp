@@ -51,12 +51,45 @@ struct DecodeArgs {
   HeadList hl;
 };
 
+// Backward arguments (kernel argument block, passed by value).
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;        // forward output
+  const void* d_o;      // gradient of the loss with respect to o
+  const float* lse;     // [B][Hq][L] natural-log denominators of the forward, sink included
+  const float* sink;    // [Hq] or NULL
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsink;         // [Hq] or NULL (sink gradient not wanted)
+  float* D;             // workspace [B][Hq][L]: <dO_i, O_i>
+  float* sink_part;     // workspace [Hq][B][n_qtiles] per-tile partial sums, NULL if no dsink
+  int B, L, Hq, Hkv, G;
+  int window;           // clamped to <= L by the host
+  float scale;
+  float scale_log2;     // scale * log2(e)
+  int heads_per_wg;     // dq kernel: query heads per workgroup
+  int n_qblocks;        // dq kernel: query blocks per (b, g, head chunk)
+  int n_hchunks;        // dq kernel: G / heads_per_wg
+  int n_kblocks;        // dk/dv kernel: key blocks per (b, g)
+  int n_qtiles;         // ceil(L / 32)
+  HeadList hl;
+};
+
 // Fills table[p][i] = (cos, sin)(p * base^(-2i/64)), p < n_pos, i < 32, evaluated in fp64.
 hipError_t rope_table_launch(int n_pos, double base, float* table, hipStream_t stream);
 // Picks the prefill variant (fills the tiling fields of `a`) and launches it on `stream`.
 hipError_t prefill_launch(bool bf16, PrefillArgs a, hipStream_t stream);
 // Launches the decode kernel and, when a.nsplit > 1, the combine kernel on `stream`.
 hipError_t decode_launch(bool bf16, const DecodeArgs& a, hipStream_t stream);
+// Launches the dq, dk/dv and sink-gradient kernels on `stream` (a.D / a.sink_part point into the
+// caller's workspace).
+hipError_t backward_launch(bool bf16, BackwardArgs a, hipStream_t stream);
+// Workspace bytes of the backward pass: D, then (256-byte aligned) the sink partials.
+size_t backward_ws_d_bytes(int B, int L, int Hq);
+size_t backward_ws_bytes(int B, int L, int Hq);
 // Workspace bytes for nsplit > 1 partial records (0 otherwise).
 size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit);
 

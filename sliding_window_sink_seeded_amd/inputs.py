@@ -37,6 +37,7 @@ STREAM_IDS = {
     "v_cache": 7,
     "cache_len": 8,
     "cache_offset": 9,
+    "d_o": 10,
 }
 
 
@@ -143,6 +144,11 @@ def prefill_inputs(seed, B, L, Hq, Hkv, dqk, dv, window, dtype="bf16", with_sink
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
     return PrefillInputs(dtype, q, k, v, sink, float(scale), int(window))
+
+
+def output_grad(seed, B, L, Hq, dv, dtype="bf16", threads=None) -> np.ndarray:
+    """Seeded upstream gradient dO [B, L, Hq, dv] of the prefill output (N(0,1), own stream)."""
+    return normal(seed, "d_o", (B, L, Hq, dv), dtype, threads)
 
 
 def decode_inputs(seed, B, T, Hq, Hkv, dqk, dv, C, window, dtype="bf16", cache_len=None,

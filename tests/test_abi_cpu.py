@@ -204,3 +204,47 @@ def decode_rope(lib, table=P, positions=1004, rot=64, max_len=1000, T=4):
 ])
 def test_decode_rope_validation(lib, kw, code):
     assert decode_rope(lib, **kw) == code
+
+
+# ------------------------------------------------------------------------------- backward pass
+
+def backward(lib, dt=BF16, B=1, L=64, Hq=64, Hkv=8, dqk=192, dv=128, lse=P, d_o=P, sink=None,
+             dsink=None, dq=P, ws=P, ws_bytes=1 << 30, scale=0.07, window=128, kvm=None):
+    return lib.mimo_attn_prefill_backward(dt, B, L, Hq, Hkv, dqk, dv, P, P, P, P, lse, d_o, window,
+                                          sink, kvm, scale, dq, P, P, dsink, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), EUNSUPPORTED),
+    (dict(L=0), EINVAL),
+    (dict(Hq=60), EINVAL),
+    (dict(dqk=128), EUNSUPPORTED),
+    (dict(window=0), EINVAL),
+    (dict(scale=0.0), EINVAL),
+    (dict(lse=None), EINVAL),             # the forward's lse is required
+    (dict(d_o=None), EINVAL),
+    (dict(dq=None), EINVAL),
+    (dict(dq=P_MIS), EINVAL),
+    (dict(lse=ctypes.c_void_p(0x10002)), EINVAL),
+    (dict(dsink=P), EINVAL),              # a sink gradient without a sink
+    (dict(ws=None), EINVAL),
+    (dict(ws=P_MIS), EINVAL),
+    (dict(ws_bytes=100), EWORKSPACE),
+])
+def test_backward_validation(lib, kw, code):
+    assert backward(lib, **kw) == code
+    assert mimo.last_error() != ""
+
+
+def test_backward_workspace_size(lib):
+    # D: B * Hq * L floats rounded up to 256 bytes, then Hq * B * ceil(L / 32) sink partials
+    assert mimo.backward_workspace_size(2, 100, 8) == 6400 + 8 * 2 * 4 * 4
+    assert mimo.backward_workspace_size(1, 33, 3) == 512 + 3 * 1 * 2 * 4
+    assert mimo.backward_workspace_size(0, 100, 8) == 0
+    # exactly the size query passes the workspace check: the call then fails only on the head map,
+    # which is checked after it
+    n = mimo.backward_workspace_size(1, 64, 4)
+    keep, bad_map = _kv_map([0, 0, 0, 1])
+    assert backward(lib, Hq=4, Hkv=2, ws_bytes=n - 1, kvm=bad_map) == EWORKSPACE
+    assert backward(lib, Hq=4, Hkv=2, ws_bytes=n, kvm=bad_map) == EINVAL
+    assert "KV head" in mimo.last_error()
