@@ -13,8 +13,8 @@ timed steps. One JSON line goes to stdout, with:
 * cpu_baseline - the float64 oracle timed on the host on a bounded leading slice of the same
   workload (a reported baseline, not a target);
 * secondary - the other measured workloads (fp32 prefill, global prefill, ring decode, split-KV
-  global decode, both decodes at the 16K-context / 64-sequence MTP setting, and the four bf16
-  workloads with the rotary embedding fused),
+  global decode, both decodes at the 16K-context / 64-sequence MTP setting, the four bf16
+  workloads with the rotary embedding fused, and the backward pass of both bf16 prefills),
   timed the same way, with decode inputs rotated over enough copies to defeat the 256 MiB MALL.
 """
 
@@ -57,8 +57,9 @@ class Case:
         self.mimo = mimo
         dt = w.dtype
         t0 = time.perf_counter()
-        if w.kind == "prefill":
+        if w.kind in ("prefill", "backward"):
             self.inp = inputs.prefill_inputs(w.seed, w.B, w.L, w.Hq, w.Hkv, w.dqk, w.dv, w.window, dt)
+            self.d_o = inputs.output_grad(w.seed, w.B, w.L, w.Hq, w.dv, dt) if w.kind == "backward" else None
             self.lens = None
             self.flops, self.bytes = workloads.algorithmic(w)
         else:
@@ -79,7 +80,19 @@ class Case:
             n_pos = w.L if w.kind == "prefill" else int(w.P or w.len_range[1]) + w.T
             self.rope = mimo.rope_table(n_pos, w.rope_base)
         self.sets = []
-        if w.kind == "prefill":
+        if w.kind == "backward":
+            # the forward's o and lse are inputs of the backward: computed once, untimed
+            base = [up(self.inp.q), up(self.inp.k), up(self.inp.v)]
+            self.d_o_t = up(self.d_o)
+            o, lse = mimo.prefill(base[0], base[1], base[2], w.window, sink=self.sink,
+                                  scale=self.inp.scale, return_lse=True)
+            self.fwd = (o, lse)
+            self.ws = torch.empty(mimo.backward_workspace_size(w.B, w.L, w.Hq), dtype=torch.uint8,
+                                  device="cuda")
+            for i in range(n_sets):
+                ts = base if i == 0 else [t.clone() for t in base]
+                self.sets.append((ts, tuple(torch.empty_like(t) for t in ts)))
+        elif w.kind == "prefill":
             base = [up(self.inp.q), up(self.inp.k), up(self.inp.v)]
             for i in range(n_sets):
                 ts = base if i == 0 else [t.clone() for t in base]
@@ -106,6 +119,10 @@ class Case:
         ts, o = self.sets[self.i % self.n_sets]
         self.i += 1
         w = self.w
+        if w.kind == "backward":
+            return self.mimo.prefill_backward(ts[0], ts[1], ts[2], self.fwd[0], self.fwd[1], self.d_o_t,
+                                              w.window, sink=self.sink, scale=self.inp.scale,
+                                              workspace=self.ws, out=o)
         if w.kind == "prefill":
             self.mimo.prefill(ts[0], ts[1], ts[2], w.window, sink=self.sink, scale=self.inp.scale, out=o,
                               rope=self.rope)
@@ -151,7 +168,17 @@ class Case:
         self.i = 0  # every rotated set holds the same inputs; use the first
         o = self.run()
         torch.cuda.synchronize()
-        if w.kind == "prefill":
+        if w.kind == "backward":
+            # dq of a few rows (all heads); the oracle reads only the sequences they lie in
+            dq = o[0]
+            rows = [(0, 0), (0, min(w.L - 1, 128)), (w.B - 1, w.L // 2), (w.B - 1, w.L - 1)]
+            got, ref = [], []
+            for b, i in rows:
+                args = [as_float(x[b:b + 1], dt) for x in (inp.q, inp.k, inp.v, self.d_o)]
+                ref.append(oracle.backward_rows(*args, w.window, inp.sink, inp.scale, [(0, i)])[0])
+                got.append(dq[b, i].float().cpu().numpy())
+            got, ref = np.stack(got), np.stack(ref)
+        elif w.kind == "prefill":
             rng = np.random.default_rng(0)
             pos = sorted({0, w.L - 1, min(w.L - 1, 127), min(w.L - 1, 128),
                           *rng.integers(0, w.L, n_rows - 4).tolist()})
@@ -206,11 +233,16 @@ def cpu_baseline(case, target_s=12.0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = 1
-    if w.kind == "prefill":
+    per_score = 2 * (3 * w.dqk + 2 * w.dv) if w.kind == "backward" else 2 * (w.dqk + w.dv)
+    if w.kind in ("prefill", "backward"):
         def run(S):
             q, k, v = (as_float(x[0:1, :S], dt) for x in (inp.q, inp.k, inp.v))
             t0 = time.perf_counter()
-            oracle.prefill(q, k, v, w.window, inp.sink, inp.scale)
+            if w.kind == "backward":
+                oracle.prefill_backward(q, k, v, as_float(case.d_o[0:1, :S], dt), w.window, inp.sink,
+                                        inp.scale)
+            else:
+                oracle.prefill(q, k, v, w.window, inp.sink, inp.scale)
             return time.perf_counter() - t0, workloads.prefill_scores(1, S, w.Hq, min(w.window, S))
 
         S = min(w.L, 512)
@@ -220,7 +252,7 @@ def cpu_baseline(case, target_s=12.0):
             S2 = int(min(w.L, max(S, S * math.sqrt(target_s / max(t, 1e-3)))))
         S2 = max(1, (S2 // 256) * 256) if S2 >= 256 else S2
         t, scores = run(S2)
-        flops = scores * 2 * (w.dqk + w.dv)
+        flops = scores * per_score
         sample = f"sequence 0, query positions [0, {S2}) of {w.L}, all {w.Hq} heads"
     else:
         def run(nseq):
@@ -246,7 +278,8 @@ def kernel_source_digest(kind):
     """sha256 over the HIP sources (names and bytes) that build and launch the `kind` kernels."""
     import hashlib
 
-    names = ["api.hip", "common.hpp", "launch.hpp", "prefill.hip" if kind == "prefill" else "decode.hip"]
+    own = {"prefill": ["tiles.hpp", "prefill.hip"], "backward": ["tiles.hpp", "backward.hip"]}
+    names = ["api.hip", "common.hpp", "launch.hpp"] + own.get(kind, ["decode.hip"])
     h = hashlib.sha256()
     for name in names:
         h.update(name.encode())
@@ -333,10 +366,10 @@ def main():
     log(f"[bench] {w.name}: {head}")
     parity = None if args.no_parity else case.sampled_parity()
 
-    if w.kind == "prefill" and w.window < w.L:
+    if w.kind in ("prefill", "backward") and w.window < w.L:
         bound, unit = "hbm", "GB/s"
         achieved, peak, per_launch = case.bytes / (event_ms * 1e-3) / 1e9, HBM_PEAK_GBS, case.bytes
-    elif w.kind == "prefill":
+    elif w.kind in ("prefill", "backward"):
         bound, unit = "mfma", "TFLOP/s"
         achieved, peak, per_launch = case.flops / (event_ms * 1e-3) / 1e12, MFMA_PEAK_TFLOPS[w.dtype], case.flops
     else:
@@ -354,7 +387,8 @@ def main():
     if not args.no_secondary:
         for name in ("swa_prefill_f32", "ga_prefill_bf16", "swa_decode_bf16", "ga_decode_bf16",
                      "swa_decode_mtp_bf16", "ga_decode_mtp_bf16", "swa_prefill_rope_bf16",
-                     "ga_prefill_rope_bf16", "swa_decode_rope_bf16", "ga_decode_rope_bf16"):
+                     "ga_prefill_rope_bf16", "swa_decode_rope_bf16", "ga_decode_rope_bf16",
+                     "swa_backward_bf16", "ga_backward_bf16"):
             if name == w.name:
                 continue
             c = Case(workloads.WORKLOADS[name])

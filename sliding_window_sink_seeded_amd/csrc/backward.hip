@@ -281,65 +281,70 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
     if (tid < 2 * kQT) reinterpret_cast<float*>(stage + St::kQBytes + St::kOBytes)[tid] = lr;
   };
 
-  f32x16 acck[kDQK / 32], accv[kDV / 32];
-#pragma unroll
-  for (int t = 0; t < kDQK / 32; ++t) acck[t] = zero16();
-#pragma unroll
-  for (int t = 0; t < kDV / 32; ++t) accv[t] = zero16();
-
   const float c = a.scale_log2;
   load_step(0);
   store_step(smem);
   wait_all();
   __syncthreads();
 
-  for (int step = 0; step < nsteps; ++step) {
-    if (step + 1 < nsteps) load_step(step + 1);
+  // One step: S = Q K^T and dP = dO V^T for the staged (head, query tile), then P, dS and the
+  // dV / dK contributions. A wave none of whose keys the tile sees computes with p = 0 (no
+  // branch: branches inside the loop make the compiler move the accumulators between register
+  // files on every step).
+  f32x16 acck[kDQK / 32], accv[kDV / 32];
+  auto compute = [&](int step, bool first) {
     const int q0 = (qt0 + step % ntiles) * kQT;
-    const bool skip = (kw0 >= a.L) || (q0 + kQT - 1 < kw0) || (q0 > kw0 + 31 + a.window - 1);
-    if (!skip) {
-      const char* stage = smem + (step & 1) * St::kBytes;
-      const char* sq = stage;
-      const char* so = stage + St::kQBytes;
-      const float* sl = reinterpret_cast<const float*>(stage + St::kQBytes + St::kOBytes);
-      const bool need_mask =
-          !((q0 >= kw0 + 31) && (q0 + kQT - 1 - kw0 < a.window) && (q0 + kQT - 1 < a.L));
+    const bool active = (kw0 < a.L) && (q0 + kQT - 1 >= kw0) && (q0 <= kw0 + 31 + a.window - 1);
+    const unsigned wlim = active ? (unsigned)a.window : 0u;  // no visible key when inactive
+    const char* stage = smem + (step & 1) * St::kBytes;
+    const char* sq = stage;
+    const char* so = stage + St::kQBytes;
+    const float* sl = reinterpret_cast<const float*>(stage + St::kQBytes + St::kOBytes);
 
-      f32x16 s = zero16(), dp = zero16();
+    f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int kk = 0; kk < kDQK / 16; ++kk) s = mma(lds_row_frag<E>(sq, St::kQS, col, kk, half), kf[kk], s);
+    for (int kk = 0; kk < kDQK / 16; ++kk) s = mma(lds_row_frag<E>(sq, St::kQS, col, kk, half), kf[kk], s);
 #pragma unroll
-      for (int kk = 0; kk < kDV / 16; ++kk) dp = mma(lds_row_frag<E>(so, St::kOS, col, kk, half), vf[kk], dp);
+    for (int kk = 0; kk < kDV / 16; ++kk) dp = mma(lds_row_frag<E>(so, St::kOS, col, kk, half), vf[kk], dp);
 
-      // register r holds query row 8 (r / 4) + 4 half + r % 4 of the tile
+    // register r holds query row 8 (r / 4) + 4 half + r % 4 of the tile
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 8 * gq + 4 * half);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + kQT + 8 * gq + 4 * half);
+    for (int gq = 0; gq < 4; ++gq) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 8 * gq + 4 * half);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + kQT + 8 * gq + 4 * half);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * gq + i;
-          float p = fast_exp2(__builtin_fmaf(s[r], c, -l4[i]));
-          if (need_mask) {
-            const int qp = q0 + 8 * gq + 4 * half + i;
-            const int d = qp - kpos;
-            p = (d >= 0 && d < a.window && qp < a.L) ? p : 0.f;
-          }
-          s[r] = p;
-          dp[r] = p * (dp[r] - d4[i]);
-        }
-      }
-#pragma unroll
-      for (int ks = 0; ks < kQT / 16; ++ks) {
-        const Frag pf = frag_from_acc<E>(s, 8 * ks);
-#pragma unroll
-        for (int t = 0; t < kDV / 32; ++t) accv[t] = mma(lds_t_frag<E>(so, St::kOS, t, ks, lane), pf, accv[t]);
-        const Frag dsf = frag_from_acc<E>(dp, 8 * ks);
-#pragma unroll
-        for (int t = 0; t < kDQK / 32; ++t) acck[t] = mma(lds_t_frag<E>(sq, St::kQS, t, ks, lane), dsf, acck[t]);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * gq + i;
+        const int qp = q0 + 8 * gq + 4 * half + i;
+        const bool vis = (unsigned)(qp - kpos) < wlim && qp < a.L;
+        // select the exponent, not the result: exp2(-inf) = 0 needs no branch
+        const float p = fast_exp2(vis ? __builtin_fmaf(s[r], c, -l4[i]) : -INFINITY);
+        s[r] = p;
+        dp[r] = p * (dp[r] - d4[i]);
       }
     }
-    if (step + 1 < nsteps) store_step(smem + ((step + 1) & 1) * St::kBytes);
+#pragma unroll
+    for (int ks = 0; ks < kQT / 16; ++ks) {
+      const Frag pf = frag_from_acc<E>(s, 8 * ks);
+#pragma unroll
+      for (int t = 0; t < kDV / 32; ++t)
+        accv[t] = mma(lds_t_frag<E>(so, St::kOS, t, ks, lane), pf, (first && ks == 0) ? zero16() : accv[t]);
+      const Frag dsf = frag_from_acc<E>(dp, 8 * ks);
+#pragma unroll
+      for (int t = 0; t < kDQK / 32; ++t)
+        acck[t] = mma(lds_t_frag<E>(sq, St::kQS, t, ks, lane), dsf, (first && ks == 0) ? zero16() : acck[t]);
+    }
+  };
+
+  // step 0 is peeled so that the accumulators start as MFMA results
+  load_step(min(1, nsteps - 1));
+  compute(0, true);
+  store_step(smem + St::kBytes);
+  __syncthreads();
+  for (int step = 1; step < nsteps; ++step) {
+    load_step(min(step + 1, nsteps - 1));
+    compute(step, false);
+    store_step(smem + ((step + 1) & 1) * St::kBytes);
     __syncthreads();
   }
 

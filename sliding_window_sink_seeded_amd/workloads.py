@@ -7,7 +7,11 @@ as the self-speculative draft), and the global decode runs at the 256K context o
 
 Algorithmic work counts only what the method must do:
 * FLOPs: 2 * (dqk + dv) per visible (query, key) score; nothing masked or skipped is counted.
+  The backward pass counts five products per visible score, 2 * (3 dqk + 2 dv): the scores
+  q.k (recomputed, as every attention backward that does not store P does), dO.v, and the
+  contributions to dV, dK and dQ.
 * Bytes: Q read once, the union of visible K/V read once, new K/V read once, O written once.
+  Backward: Q, K, V, O, dO and lse read once, dQ, dK, dV written once.
 """
 
 from __future__ import annotations
@@ -21,7 +25,7 @@ import numpy as np
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "prefill" or "decode"
+    kind: str  # "prefill", "decode" or "backward" (of a prefill)
     dtype: str  # "f32" or "bf16"
     Hq: int
     Hkv: int
@@ -78,6 +82,15 @@ WORKLOADS = {
         description="global decode bf16, 64 seqs x 16384 cached + 4 tokens, 64/4 heads, split-KV"),
 }
 
+# The training backward pass of the two bf16 prefill workloads (MiMo-V2-Flash Technical Report
+# review (xllm-io), §3.2: the sink logit is learned, so its gradient is computed too).
+WORKLOADS["swa_backward_bf16"] = Workload(
+    "swa_backward_bf16", "backward", "bf16", 64, 8, 128, B=4, L=32768, seed=2,
+    description="sliding-window backward bf16 (dq, dk, dv, dsink), batch 4 x 32768, 64/8 heads, W=128")
+WORKLOADS["ga_backward_bf16"] = Workload(
+    "ga_backward_bf16", "backward", "bf16", 64, 4, 32768, B=1, L=32768, seed=3,
+    description="global causal backward bf16 (dq, dk, dv, dsink), batch 1 x 32768, 64/4 heads")
+
 # The same four bf16 workloads with Q/K given before the rotary embedding, rotated inside the
 # kernels (MiMo-V2-Flash Technical Report review (xllm-io), §3.1 and §4: first 64 dims, base 10K for
 # sliding-window layers, 5M for global layers). Same inputs (same seeds) as the plain workloads.
@@ -122,9 +135,20 @@ def decode_bytes(w: Workload, lens: np.ndarray) -> int:
     return q + cache + new + o
 
 
+def backward_bytes(w: Workload) -> int:
+    e = w.elem
+    per_row = w.Hq * (w.dqk + 2 * w.dv) * e + w.Hq * 4  # reads: q, o, dO, lse
+    per_row += w.Hkv * (w.dqk + w.dv) * e                # reads: k, v
+    per_row += w.Hq * w.dqk * e + w.Hkv * (w.dqk + w.dv) * e  # writes: dq, dk, dv
+    return w.B * w.L * per_row
+
+
 def algorithmic(w: Workload, lens: np.ndarray | None = None) -> tuple[int, int]:
     """(FLOPs, bytes) of one pass over workload ``w`` (decode needs the drawn lengths)."""
     per_score = 2 * (w.dqk + w.dv)
+    if w.kind == "backward":
+        return (prefill_scores(w.B, w.L, w.Hq, w.window) * 2 * (3 * w.dqk + 2 * w.dv),
+                backward_bytes(w))
     if w.kind == "prefill":
         return prefill_scores(w.B, w.L, w.Hq, w.window) * per_score, prefill_bytes(w)
     return decode_scores(lens, w.T, w.Hq, w.window) * per_score, decode_bytes(w, lens)
