@@ -265,10 +265,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
     for (int i = 0; i < QPT; ++i) qr[i] = ld16(qp + 16 * (spart * QPT + i));
 #pragma unroll
     for (int i = 0; i < OPT; ++i) orr[i] = ld16(op + 16 * (spart * OPT + i));
-    if (tid < 2 * kQT) {
+    {  // every thread loads (threads past 64 re-read a D entry): no branch and no use of the
+       // value before store_step, so nothing waits for this load here
       const int r = min(q0 + (tid & 31), a.L - 1);
       const size_t li = ((size_t)b * a.Hq + head) * a.L + r;
-      lr = tid < kQT ? a.lse[li] * kLog2e : a.D[li];
+      lr = (tid < kQT ? a.lse : a.D)[li];
     }
   };
   auto store_step = [&](char* stage) {
@@ -278,7 +279,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
     for (int i = 0; i < QPT; ++i) st16(sq + 16 * i, qr[i]);
 #pragma unroll
     for (int i = 0; i < OPT; ++i) st16(so + 16 * i, orr[i]);
-    if (tid < 2 * kQT) reinterpret_cast<float*>(stage + St::kQBytes + St::kOBytes)[tid] = lr;
+    if (tid < 2 * kQT)
+      reinterpret_cast<float*>(stage + St::kQBytes + St::kOBytes)[tid] = tid < kQT ? lr * kLog2e : lr;
   };
 
   const float c = a.scale_log2;
@@ -336,14 +338,20 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
     }
   };
 
-  // step 0 is peeled so that the accumulators start as MFMA results
+  // Step 0 is peeled so that the accumulators start as MFMA results. The scheduling barriers
+  // keep the next step's loads ahead of the math and its LDS stores behind it (left alone, the
+  // scheduler pulls the stores up next to the loads and every step waits for global memory).
   load_step(min(1, nsteps - 1));
+  __builtin_amdgcn_sched_barrier(0);
   compute(0, true);
+  __builtin_amdgcn_sched_barrier(0);
   store_step(smem + St::kBytes);
   __syncthreads();
   for (int step = 1; step < nsteps; ++step) {
     load_step(min(step + 1, nsteps - 1));
+    __builtin_amdgcn_sched_barrier(0);
     compute(step, false);
+    __builtin_amdgcn_sched_barrier(0);
     store_step(smem + ((step + 1) & 1) * St::kBytes);
     __syncthreads();
   }
