@@ -82,8 +82,9 @@ size_t mimo_attn_decode_workspace_size(int B, int T, int Hq, int Hkv, int d_v, i
                                        int window, int num_splits);
 
 /*
- * Decode / MTP verification: T new tokens per sequence (the next token plus up to three drafts,
- * MiMo series notes, MiMo-V2-Flash > lightweight MTP > inference), attending to committed cache
+ * Decode / MTP verification: T new tokens per sequence (the next token plus up to seven drafts:
+ * three MTP drafts, MiMo series notes, MiMo-V2-Flash > lightweight MTP > inference, or a block
+ * draft of 6 or 8 tokens, same notes, MiMo-V2.6 decoding ablation), attending to committed cache
  * entries and, causally, to each other.
  *
  *   q       [B, T, Hq,  d_qk]            k_new [B, T, Hkv, d_qk]   v_new [B, T, Hkv, d_v]
@@ -100,7 +101,7 @@ size_t mimo_attn_decode_workspace_size(int B, int T, int Hq, int Hkv, int d_v, i
  *   workspace / workspace_bytes: device scratch of at least mimo_attn_decode_workspace_size(...)
  *   bytes (may be NULL when that size is 0). Its contents are overwritten.
  *
- * Errors: MIMO_EINVAL for sizes < 1, T outside 1..4, Hq % Hkv != 0, a bad head map, window < 1,
+ * Errors: MIMO_EINVAL for sizes < 1, T outside 1..8, Hq % Hkv != 0, a bad head map, window < 1,
  * max_cache_len < 0, a cache too small for the window (C < min(window - 1, max_cache_len)),
  * num_splits < 0, NULL or misaligned pointers; MIMO_EWORKSPACE when the workspace is too small;
  * MIMO_EUNSUPPORTED for other head dims or dtypes; MIMO_EHIP if a launch fails.
@@ -156,6 +157,35 @@ int mimo_attn_decode_rope(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk
                           const float* rope_table, int rope_positions, int rot_dims,
                           int num_splits, void* workspace, size_t workspace_bytes, void* o,
                           float* lse, hipStream_t stream);
+
+/*
+ * Commit after a verify step: for every sequence b, the first n_b of its T new tokens (the
+ * accepted prefix, n_b = accept_len[b] clamped to [0, T], all T when accept_len is NULL) are
+ * written to the cache at positions P_b .. P_b + n_b - 1, P_b = cache_len[b], i.e. to slots
+ * (p + cache_offset[b]) mod C - the layout mimo_attn_decode reads - and cache_len[b] becomes
+ * P_b + n_b (on the device, ordered on `stream` after any earlier decode). Rejected drafts are
+ * rolled back by never being written: afterwards the cache is that of the accepted sequence.
+ * (MiMo series notes (plmsmile), MiMo-V2-Flash > lightweight MTP > inference: only drafts the
+ * main model accepts continue the sequence; jienda explainer §4.3: fixed-size cache for the
+ * sliding-window layers.)
+ *
+ *   k_new [B, T, Hkv, d_qk], v_new [B, T, Hkv, d_v] dtype dt: the verify step's new K / V.
+ *   k_cache [B, C, Hkv, d_qk], v_cache [B, C, Hkv, d_v]: updated in place.
+ *   cache_len [B] int32 device: read and advanced. cache_offset [B] int32 device, nullable (0).
+ *   accept_len [B] int32 device, nullable.
+ *   max_cache_len: the cache never holds more positions: n_b is also clamped to
+ *   max_cache_len - P_b. A linear (global-layer) cache holds positions < C, so pass
+ *   max_cache_len <= C for it; a sliding-window ring of C >= window - 1 slots may take any
+ *   max_cache_len, the oldest positions being overwritten.
+ *
+ * Errors: MIMO_EINVAL for B, Hkv, C < 1, T outside 1..8, max_cache_len outside [0, 2^30 - 8],
+ * NULL or misaligned pointers; MIMO_EUNSUPPORTED for other head dims or dtypes; MIMO_EHIP if the
+ * launch fails. cache_len entries outside [0, max_cache_len] are clamped into it first.
+ */
+int mimo_attn_cache_append(mimo_dtype dt, int B, int T, int Hkv, int d_qk, int d_v,
+                           const void* k_new, const void* v_new, void* k_cache, void* v_cache, int C,
+                           int32_t* cache_len, const int32_t* cache_offset,
+                           const int32_t* accept_len, int max_cache_len, hipStream_t stream);
 
 /*
  * Backward pass of mimo_attn_prefill: gradients of a scalar loss with respect to q, k, v and the

@@ -10,6 +10,7 @@ fallback. If the shared library is missing, every call raises.
     table = rope_table(n_pos, base=1e4)                        # RoPE (cos, sin), device fp32
     o, lse = prefill(q, k, v, 128, sink=sink, rope=table)      # q, k given before RoPE
     dq, dk, dv, dsink = prefill_backward(q, k, v, o, lse, do, 128, sink=sink)
+    cache_append(k_new, v_new, k_cache, v_cache, cache_len, max_len, accept=accepted)
 """
 
 from __future__ import annotations
@@ -18,7 +19,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["prefill", "decode", "decode_workspace_size", "rope_table", "prefill_backward",
+__all__ = ["prefill", "decode", "decode_workspace_size", "rope_table", "prefill_backward", "cache_append",
            "backward_workspace_size", "last_error", "version", "library", "LIB_PATH", "MimoError",
            "EXPORTS", "ROPE_DIMS"]
 
@@ -26,6 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmimo_att
 EXPORTS = ("mimo_attn_prefill", "mimo_attn_decode", "mimo_attn_decode_workspace_size",
            "mimo_attn_rope_table", "mimo_attn_prefill_rope", "mimo_attn_decode_rope",
            "mimo_attn_prefill_backward", "mimo_attn_prefill_backward_workspace_size",
+           "mimo_attn_cache_append",
            "mimo_attn_last_error", "mimo_attn_version")
 ROPE_DIMS = 64  # rotated leading Q/K dims
 
@@ -74,6 +76,9 @@ def library() -> ctypes.CDLL:
     lib.mimo_attn_prefill_backward.restype = i32
     lib.mimo_attn_prefill_backward_workspace_size.argtypes = [i32, i32, i32]
     lib.mimo_attn_prefill_backward_workspace_size.restype = sz
+    lib.mimo_attn_cache_append.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp,
+                                            vp, i32, vp]
+    lib.mimo_attn_cache_append.restype = i32
     lib.mimo_attn_last_error.argtypes = []
     lib.mimo_attn_last_error.restype = ctypes.c_char_p
     lib.mimo_attn_version.argtypes = []
@@ -331,3 +336,33 @@ def prefill_backward(q, k, v, o, lse, d_o, window: int, sink=None, scale: float 
     del keep
     _check(rc)
     return dq, dk, dv, dsink
+
+
+def cache_append(k_new, v_new, k_cache, v_cache, cache_len, max_cache_len: int, cache_offset=None,
+                 accept=None, stream=None):
+    """Commit the accepted prefix of a verify step's T new tokens into the cache, in place.
+
+    k_new/v_new [B, T, Hkv, d]; k_cache/v_cache [B, C, Hkv, d]; cache_len int32 [B] (advanced on
+    the device); cache_offset, accept: int32 [B] GPU tensors or None (offset 0 / all T accepted).
+    Returns cache_len.
+    """
+    import torch
+
+    _dev(k_new, "k_new", ndim=4)
+    dt = _dtype_code(k_new)
+    for name, t in (("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(t, name, k_new.dtype, 4)
+    B, T, Hkv, dqk = k_new.shape
+    dv, C = v_new.shape[3], k_cache.shape[1]
+    if (tuple(v_new.shape[:3]) != (B, T, Hkv) or tuple(k_cache.shape) != (B, C, Hkv, dqk)
+            or tuple(v_cache.shape) != (B, C, Hkv, dv)):
+        raise ValueError("cache_append tensor shapes disagree")
+    _dev(cache_len, "cache_len", torch.int32, 1)
+    for name, t in (("cache_offset", cache_offset), ("accept", accept)):
+        if t is not None:
+            _dev(t, name, torch.int32, 1)
+    _check(library().mimo_attn_cache_append(dt, B, T, Hkv, dqk, dv, _ptr(k_new), _ptr(v_new),
+                                            _ptr(k_cache), _ptr(v_cache), C, _ptr(cache_len),
+                                            _ptr(cache_offset), _ptr(accept), int(max_cache_len),
+                                            _stream(stream)))
+    return cache_len

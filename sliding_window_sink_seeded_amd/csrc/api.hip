@@ -134,6 +134,36 @@ int mimo_attn_prefill_rope(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_q
                       rope_table, o, lse, stream);
 }
 
+int mimo_attn_cache_append(mimo_dtype dt, int B, int T, int Hkv, int d_qk, int d_v,
+                           const void* k_new, const void* v_new, void* k_cache, void* v_cache, int C,
+                           int32_t* cache_len, const int32_t* cache_offset,
+                           const int32_t* accept_len, int max_cache_len, hipStream_t stream) {
+  g_err.clear();
+  if (dt != MIMO_F32 && dt != MIMO_BF16) return fail(MIMO_EUNSUPPORTED, "unknown dtype %d", dt);
+  if (B < 1 || Hkv < 1) return fail(MIMO_EINVAL, "B and Hkv must be >= 1");
+  if (T < 1 || T > mimo::kMaxNew) return fail(MIMO_EINVAL, "T must be in 1..%d (got %d)", mimo::kMaxNew, T);
+  if (d_qk != 192 || d_v != 128)
+    return fail(MIMO_EUNSUPPORTED, "head dims (%d, %d) unsupported; this build has (192, 128)", d_qk, d_v);
+  if (C < 1) return fail(MIMO_EINVAL, "C must be >= 1");
+  if (max_cache_len < 0 || max_cache_len > (1 << 30) - 8)
+    return fail(MIMO_EINVAL, "max_cache_len %d outside [0, 2^30 - 8]", max_cache_len);
+  if (!k_new || !v_new || !k_cache || !v_cache || !cache_len)
+    return fail(MIMO_EINVAL, "k_new, v_new, k_cache, v_cache and cache_len must be non-NULL");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(MIMO_EINVAL, "k_new, v_new, k_cache and v_cache must be 16-byte aligned");
+  if (!aligned4(cache_len) || (cache_offset && !aligned4(cache_offset)) || (accept_len && !aligned4(accept_len)))
+    return fail(MIMO_EINVAL, "cache_len, cache_offset and accept_len must be 4-byte aligned");
+  const double elem = dt == MIMO_BF16 ? 2.0 : 4.0;
+  if ((double)B * C * Hkv * d_qk * elem > 4.6e18) return fail(MIMO_EINVAL, "cache too large");
+  mimo::AppendArgs a{};
+  a.k_new = k_new; a.v_new = v_new; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.cache_len = cache_len; a.cache_offset = cache_offset; a.accept = accept_len;
+  a.B = B; a.T = T; a.Hkv = Hkv; a.C = C; a.max_len = max_cache_len;
+  const hipError_t e = mimo::cache_append_launch(dt == MIMO_BF16, a, stream);
+  if (e != hipSuccess) return fail(MIMO_EHIP, "cache append launch failed: %s", hipGetErrorString(e));
+  return MIMO_OK;
+}
+
 size_t mimo_attn_prefill_backward_workspace_size(int B, int L, int Hq) {
   if (B < 1 || L < 1 || Hq < 1) return 0;
   return mimo::backward_ws_bytes(B, L, Hq);
@@ -223,7 +253,8 @@ DecodePlan plan_decode(int B, int T, int Hq, int Hkv, int max_len, int window, i
   if (num_splits > 0) {
     ns = num_splits;
   } else {
-    const long long pairs = (long long)B * Hkv;
+    const long long chunks = ((long long)(Hq / Hkv) * T + mimo::kMaxCols - 1) / mimo::kMaxCols;
+    const long long pairs = (long long)B * Hkv * chunks;
     const long long fill = (256 + pairs - 1) / pairs;
     const long long by_len = (list_max + 8191) / 8192;
     ns = fill > by_len ? fill : by_len;
@@ -246,8 +277,8 @@ extern "C" {
 
 size_t mimo_attn_decode_workspace_size(int B, int T, int Hq, int Hkv, int d_v, int max_cache_len,
                                        int window, int num_splits) {
-  if (B < 1 || T < 1 || T > 4 || Hq < 1 || Hkv < 1 || Hq % Hkv || d_v != 128 || max_cache_len < 0 ||
-      window < 1 || num_splits < 0 || (Hq / Hkv) * T > mimo::kMaxCols)
+  if (B < 1 || T < 1 || T > mimo::kMaxNew || Hq < 1 || Hkv < 1 || Hq % Hkv || d_v != 128 ||
+      max_cache_len < 0 || window < 1 || num_splits < 0 || Hq > mimo::kMaxHeads)
     return 0;
   return plan_decode(B, T, Hq, Hkv, max_cache_len, window, num_splits).ws_bytes;
 }
@@ -264,10 +295,7 @@ int decode_impl(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
                 const float* rope, int num_splits, void* workspace, size_t workspace_bytes,
                 void* o, float* lse, hipStream_t stream) {
   if (int rc = check_common(dt, B, Hq, Hkv, d_qk, d_v, window, scale)) return rc;
-  if (T < 1 || T > 4) return fail(MIMO_EINVAL, "T must be in 1..4 (got %d)", T);
-  if ((Hq / Hkv) * T > mimo::kMaxCols)
-    return fail(MIMO_EUNSUPPORTED, "(Hq/Hkv) * T = %d exceeds %d query columns per KV head",
-                (Hq / Hkv) * T, mimo::kMaxCols);
+  if (T < 1 || T > mimo::kMaxNew) return fail(MIMO_EINVAL, "T must be in 1..%d (got %d)", mimo::kMaxNew, T);
   if (max_cache_len < 0 || max_cache_len > (1 << 30) - 8)
     return fail(MIMO_EINVAL, "max_cache_len %d outside [0, 2^30 - 8]", max_cache_len);
   if (C < 1) return fail(MIMO_EINVAL, "C must be >= 1");
@@ -306,6 +334,8 @@ int decode_impl(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
   a.nsplit = plan.nsplit;
   a.keys_per_split = plan.keys_per_split;
   a.ncols = a.G * T;
+  a.n_chunks = (a.ncols + mimo::kMaxCols - 1) / mimo::kMaxCols;
+  if ((long long)a.Hkv * a.n_chunks > 65535) return fail(MIMO_EUNSUPPORTED, "too many KV heads x column chunks");
   if (int rc = group_heads(Hq, Hkv, kv_head_of_q, &a.hl)) return rc;
   const hipError_t e = mimo::decode_launch(dt == MIMO_BF16, a, stream);
   if (e != hipSuccess) return fail(MIMO_EHIP, "decode launch failed: %s", hipGetErrorString(e));

@@ -8,15 +8,17 @@
 //
 // Keys of sequence b: committed positions [max(0, P - W + 1), P) read from slot (p + off) mod C,
 // and the T new tokens at positions P .. P+T-1. New token t sees positions in [P + t - W + 1,
-// P + t]. The committed keys are processed in 32-key MFMA blocks; the new tokens (at most 4) are
-// folded in afterwards by the last split, new token w by wave w, as one extra key per column
-// computed on the VALU (bf16 dot2). For a 128-key window this keeps the committed keys at exactly
-// four blocks, one per wave, instead of a fifth, nearly empty block on one wave.
+// P + t]. The committed keys are processed in 32-key MFMA blocks; the new tokens (at most 8: the
+// next token plus drafts, e.g. blocks of 6 or 8) are folded in afterwards by the last split, new
+// token t by wave t % 4, as one extra key per column computed on the VALU (bf16 dot2). For a
+// 128-key window this keeps the committed keys at exactly four blocks, one per wave, instead of a
+// fifth, nearly empty block on one wave.
 //
-// Work decomposition: one workgroup per (split, KV head g, sequence b). The G*T query columns of
-// (b, g) - every query head of the group times every new token - are the MFMA columns (32 per
-// column block), so each K/V element read from HBM serves all of them; Q^T sits in LDS, shared
-// by the waves. The split's keys are cut into 32-key blocks dealt round-robin to the waves. Lane
+// Work decomposition: one workgroup per (split, KV head g, column chunk, sequence b). The G*T query
+// columns of (b, g) - every query head of the group times every new token - are the MFMA columns
+// (32 per column block, at most two blocks per workgroup; more columns, e.g. 16 heads x 8 tokens,
+// are cut into chunks of 64 that run as separate workgroups), so each K/V element read from HBM
+// serves all the columns of a chunk; Q^T sits in LDS, shared by the waves. The split's keys are cut into 32-key blocks dealt round-robin to the waves. Lane
 // (col, half) of a wave fetches half of the K row and half of the V row of key key0 + col: the K
 // half is directly its MFMA A fragment, the V half goes to a wave-private LDS tile that the PV
 // product reads back transposed.
@@ -49,9 +51,9 @@ struct DecodeLds {
   static constexpr int kVBytes = (kVRowMajor ? 32 : kDDV) * kVStride * E::kBytes;
   static constexpr int kMergeBytes = kDecNW * 2 * 16 * 64 * 4;  // two dv blocks of one column block
   static constexpr int kWorkBytes = kDecNW * kVBytes > kMergeBytes ? kDecNW * kVBytes : kMergeBytes;
-  // new-token K and V rows (T <= 4), staged with Q at kernel start
-  static constexpr int kNewKBytes = 4 * kDDQK * E::kBytes;
-  static constexpr int kNewBytes = kNewKBytes + 4 * kDDV * E::kBytes;
+  // new-token K and V rows (T <= kMaxNew), staged with Q at kernel start
+  static constexpr int kNewKBytes = kMaxNew * kDDQK * E::kBytes;
+  static constexpr int kNewBytes = kNewKBytes + kMaxNew * kDDV * E::kBytes;
   static constexpr int kBytes = kQBytes + kNewBytes + kWorkBytes + kDecNW * 64 * 4 * 2;
 };
 
@@ -126,8 +128,12 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
 
   const int split = blockIdx.x;
-  const int g = blockIdx.y;
+  const int chunk = blockIdx.y % a.n_chunks;
+  const int g = blockIdx.y / a.n_chunks;
   const int b = blockIdx.z;
+  // this workgroup's query columns: cbase + [0, ncols) of the G*T columns of (b, g)
+  const int cbase = chunk * kMaxCols;
+  const int ncols = min(kMaxCols, a.ncols - cbase);
 
   int P = a.cache_len[b];
   P = P < 0 ? 0 : (P > a.max_len ? a.max_len : P);
@@ -169,11 +175,12 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
     constexpr int kQChunks = NCB * 32 * kChunksRow;
     constexpr int kQPer = (kQChunks + kDecNW * 64 - 1) / (kDecNW * 64);
     constexpr int kKCh = kDDQK / E::kPerChunk, kVCh = kDDV / E::kPerChunk;
+    // new tokens 0..3 are staged here; 4..7, when present, by a second batch below
     constexpr int kNewPer = (4 * (kKCh + kVCh) + kDecNW * 64 - 1) / (kDecNW * 64);
     int head[kQPer];
 #pragma unroll
     for (int i = 0; i < kQPer; ++i) {
-      const int c = min((tid + i * kDecNW * 64) / kChunksRow, a.ncols - 1);  // padding: any valid row
+      const int c = cbase + min((tid + i * kDecNW * 64) / kChunksRow, ncols - 1);  // padding: any valid row
       head[i] = g * a.G + c / a.T;
     }
     if (!a.hl.identity) {
@@ -184,7 +191,7 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
 #pragma unroll
     for (int i = 0; i < kQPer; ++i) {
       const int u = tid + i * kDecNW * 64;
-      const int c = min(u / kChunksRow, a.ncols - 1), ch = u % kChunksRow;
+      const int c = cbase + min(u / kChunksRow, ncols - 1), ch = u % kChunksRow;
       xq[i] = ld16((const char*)a.q + (((size_t)b * a.T + c % a.T) * a.Hq + head[i]) * krow_bytes + ch * 16);
     }
     const bool last = split == a.nsplit - 1;
@@ -207,20 +214,23 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
     for (int i = 0; i < kQPer; ++i) {
       const int u = tid + i * kDecNW * 64;
       const int c = u / kChunksRow, ch = u % kChunksRow;
-      if (u < kQChunks) st16(sq + c * Lds::kQStride * E::kBytes + ch * 16, c < a.ncols ? xq[i] : zero_chunk());
+      if (u < kQChunks) st16(sq + c * Lds::kQStride * E::kBytes + ch * 16, c < ncols ? xq[i] : zero_chunk());
     }
     char* snew = smem + Lds::kQBytes;
+    auto store_new = [&](int t0, const u32x4 (&x)[kNewPer]) {
 #pragma unroll
-    for (int i = 0; i < kNewPer; ++i) {
-      const int u = tid + i * kDecNW * 64;
-      const int t = u / (kKCh + kVCh), ch = u % (kKCh + kVCh);
-      if (last && t < a.T) {
-        if (ch < kKCh)
-          st16(snew + t * kDDQK * E::kBytes + ch * 16, xn[i]);
-        else
-          st16(snew + Lds::kNewKBytes + t * kDDV * E::kBytes + (ch - kKCh) * 16, xn[i]);
+      for (int i = 0; i < kNewPer; ++i) {
+        const int u = tid + i * kDecNW * 64;
+        const int t = t0 + u / (kKCh + kVCh), ch = u % (kKCh + kVCh);
+        if (last && u < 4 * (kKCh + kVCh) && t < a.T) {
+          if (ch < kKCh)
+            st16(snew + t * kDDQK * E::kBytes + ch * 16, x[i]);
+          else
+            st16(snew + Lds::kNewKBytes + t * kDDV * E::kBytes + (ch - kKCh) * 16, x[i]);
+        }
       }
-    }
+    };
+    store_new(0, xn);
   }
 
   int qpos[NCB];
@@ -229,7 +239,7 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int c = cb * 32 + col;
-    qpos[cb] = c < a.ncols ? P + c % a.T : -(1 << 30);  // padding columns see no key
+    qpos[cb] = c < ncols ? P + (cbase + c) % a.T : -(1 << 30);  // padding columns see no key
     m[cb] = -INFINITY;
     l[cb] = 0.f;
 #pragma unroll
@@ -261,12 +271,12 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
     // c % T) and new token t at positions P + c % T and P + t; pairs (i, i + 32), i < 32
     constexpr int kHalfRot = kRopeDims / 2;
     const bool last = split == a.nsplit - 1;
-    const int n_q = a.ncols * kHalfRot, n_k = last ? a.T * kHalfRot : 0;
+    const int n_q = ncols * kHalfRot, n_k = last ? a.T * kHalfRot : 0;
     for (int u = tid; u < n_q + n_k; u += kDecNW * 64) {
       const bool is_q = u < n_q;
       const int uu = is_q ? u : u - n_q;
       const int row = uu / kHalfRot, i = uu % kHalfRot;
-      const int pos = P + (is_q ? row % a.T : row);
+      const int pos = P + (is_q ? (cbase + row) % a.T : row);
       char* base = is_q ? sq + row * Lds::kQStride * E::kBytes : smem + Lds::kQBytes + row * kDDQK * E::kBytes;
       const f32x2 csn = *reinterpret_cast<const f32x2*>(a.rope + ((size_t)pos * kHalfRot + i) * 2);
       if constexpr (E::kBytes == 2) {
@@ -375,10 +385,28 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
     }
   }
 
-  // ---- new token `wave` (last split only): one extra key per column, on the VALU ----
-  if (split == a.nsplit - 1 && wave < a.T) {
-    const char* krow = smem + Lds::kQBytes + wave * kDDQK * E::kBytes;  // staged in LDS
-    const char* vrow = smem + Lds::kQBytes + Lds::kNewKBytes + wave * kDDV * E::kBytes;
+  // ---- block drafts (T > 4, last split): new tokens 4 .. T-1 are staged only now, when the
+  // registers of the key loop are free (staging them with the first four costs the whole kernel
+  // some 50 registers) ----
+  if (split == a.nsplit - 1 && a.T > 4) {
+    constexpr int kKCh = kDDQK / E::kPerChunk, kVCh = kDDV / E::kPerChunk;
+    char* snew = smem + Lds::kQBytes;
+    for (int u = tid; u < (a.T - 4) * (kKCh + kVCh); u += kDecNW * 64) {
+      const int t = 4 + u / (kKCh + kVCh), ch = u % (kKCh + kVCh);
+      if (ch < kKCh)
+        st16(snew + t * kDDQK * E::kBytes + ch * 16,
+             ld16((const char*)a.k_new + (((size_t)b * a.T + t) * a.Hkv + g) * krow_bytes + ch * 16));
+      else
+        st16(snew + Lds::kNewKBytes + t * kDDV * E::kBytes + (ch - kKCh) * 16,
+             ld16((const char*)a.v_new + (((size_t)b * a.T + t) * a.Hkv + g) * vrow_bytes + (ch - kKCh) * 16));
+    }
+    __syncthreads();
+  }
+
+  // ---- new tokens wave, wave + 4 (last split only): one extra key per column, on the VALU ----
+  for (int tn = wave; split == a.nsplit - 1 && tn < a.T; tn += kDecNW) {
+    const char* krow = smem + Lds::kQBytes + tn * kDDQK * E::kBytes;  // staged in LDS
+    const char* vrow = smem + Lds::kQBytes + Lds::kNewKBytes + tn * kDDV * E::kBytes;
     const float c = a.scale_log2;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
@@ -402,8 +430,8 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
       }
       dot = halves_sum(dot);
       const int ccol = cb * 32 + col;
-      const int t = ccol % a.T;
-      const bool vis = ccol < a.ncols && t >= wave && t - wave < a.window;
+      const int t = (cbase + ccol) % a.T;
+      const bool vis = ccol < ncols && t >= tn && t - tn < a.window;
       const float sc = vis ? dot * c : -INFINITY;
       update_max(cb, sc);
       const float p = fast_exp2(sc - ((m[cb] == -INFINITY) ? 0.f : m[cb]));
@@ -442,8 +470,8 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
     sm_m[wave * 64 + lane] = m[cb];
     sm_l[wave * 64 + lane] = l[cb];
     __syncthreads();
-    const int c = cb * 32 + col;
-    const bool cvalid = c < a.ncols;
+    const int c = cbase + cb * 32 + col;  // column within the G*T columns of (b, g)
+    const bool cvalid = cb * 32 + col < ncols;
     const int t = cvalid ? c % a.T : 0;
     const int head = cvalid ? a.hl.at(g * a.G + c / a.T) : 0;
     float M = -INFINITY;
@@ -498,7 +526,7 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
           a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(Lsum)) * kLn2;
       } else {
         // partial record for (b, g, split, column c): acc[kDDV], m, l
-        const int ncols_pad = NCB * 32;
+        const int ncols_pad = ((a.ncols + 31) / 32) * 32;
         float* rec = a.ws + ((((size_t)b * a.Hkv + g) * a.nsplit + split) * ncols_pad + c) * kRec;
 #pragma unroll
         for (int g2 = 0; g2 < 2; ++g2) {
@@ -582,6 +610,47 @@ __global__ __launch_bounds__(kCombCols * kDDV / 4) void combine_kernel(const Dec
   if (a.lse && quad == 0) a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(L)) * kLn2;
 }
 
+// Commits the accepted prefix of a verify step: new tokens 0 .. n_b - 1 of sequence b go to
+// positions P_b .. P_b + n_b - 1, i.e. slots (p + off_b) mod C, and cache_len[b] becomes
+// P_b + n_b. One workgroup per sequence; 16-byte chunks of K and V rows are spread over its
+// threads. Every thread reads cache_len[b] before the barrier, one thread writes it after.
+template <typename E>
+__global__ __launch_bounds__(256) void cache_append_kernel(const AppendArgs a) {
+  constexpr int kKCh = kDDQK / E::kPerChunk, kVCh = kDDV / E::kPerChunk;
+  const int b = blockIdx.x;
+  int P = a.cache_len[b];
+  P = P < 0 ? 0 : (P > a.max_len ? a.max_len : P);
+  int n = a.accept ? a.accept[b] : a.T;
+  n = n < 0 ? 0 : (n > a.T ? a.T : n);
+  n = min(n, a.max_len - P);  // the cache never holds more than max_len positions
+  const int off = a.cache_offset ? a.cache_offset[b] : 0;
+  const size_t krow_bytes = (size_t)kDDQK * E::kBytes, vrow_bytes = (size_t)kDDV * E::kBytes;
+  const int per_tok = a.Hkv * (kKCh + kVCh);
+  for (int u = threadIdx.x; u < n * per_tok; u += 256) {
+    const int t = u / per_tok, r = u % per_tok;
+    const int g = r / (kKCh + kVCh), ch = r % (kKCh + kVCh);
+    int slot = (P + t + off) % a.C;
+    slot += slot < 0 ? a.C : 0;
+    const size_t src = ((size_t)b * a.T + t) * a.Hkv + g;
+    const size_t dst = ((size_t)b * a.C + slot) * a.Hkv + g;
+    if (ch < kKCh)
+      st16((char*)a.k_cache + dst * krow_bytes + ch * 16, ld16((const char*)a.k_new + src * krow_bytes + ch * 16));
+    else
+      st16((char*)a.v_cache + dst * vrow_bytes + (ch - kKCh) * 16,
+           ld16((const char*)a.v_new + src * vrow_bytes + (ch - kKCh) * 16));
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.cache_len[b] = P + n;
+}
+
+hipError_t cache_append_launch(bool bf16, const AppendArgs& a, hipStream_t stream) {
+  if (bf16)
+    hipLaunchKernelGGL(cache_append_kernel<BF16>, dim3(a.B), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(cache_append_kernel<F32>, dim3(a.B), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit) {
   if (nsplit <= 1) return 0;
   const size_t ncols_pad = (size_t)((ncols + 31) / 32) * 32;
@@ -596,9 +665,9 @@ size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit) {
 
 template <bool ROPE>
 static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.nsplit, a.Hkv, a.B);
+  const dim3 grid(a.nsplit, a.Hkv * a.n_chunks, a.B);
   const dim3 block(kDecNW * 64);
-  const bool two = a.ncols > 32;
+  const bool two = (a.n_chunks > 1 ? kMaxCols : a.ncols) > 32;
   if (bf16 && two)
     hipLaunchKernelGGL((decode_kernel<BF16, 2, true, ROPE>), grid, block, 0, stream, a);
   else if (bf16)

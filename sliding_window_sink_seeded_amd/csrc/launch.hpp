@@ -5,7 +5,8 @@
 
 namespace mimo {
 
-constexpr int kMaxCols = 64;  // decode: query columns (query heads per KV head x new tokens)
+constexpr int kMaxCols = 64;  // decode: query columns per workgroup (query heads per KV head x new tokens)
+constexpr int kMaxNew = 8;    // decode: new tokens per sequence (next token + drafts)
 
 // Prefill arguments (kernel argument block, passed by value).
 struct PrefillArgs {
@@ -46,7 +47,8 @@ struct DecodeArgs {
   float scale_log2;
   int nsplit;
   int keys_per_split;  // multiple of 32
-  int ncols;           // G * T
+  int ncols;           // G * T query columns per KV head
+  int n_chunks;        // ceil(ncols / kMaxCols) workgroups share them
   const float* rope;   // [>= max_len + T][32][2] (cos, sin) when q/k_new arrive unrotated, else NULL
   HeadList hl;
 };
@@ -78,6 +80,18 @@ struct BackwardArgs {
   HeadList hl;
 };
 
+// Cache commit arguments (kernel argument block, passed by value).
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  int32_t* cache_len;           // [B], read then advanced
+  const int32_t* cache_offset;  // [B] or NULL
+  const int32_t* accept;        // [B] or NULL (all T)
+  int B, T, Hkv, C, max_len;
+};
+
 // Fills table[p][i] = (cos, sin)(p * base^(-2i/64)), p < n_pos, i < 32, evaluated in fp64.
 hipError_t rope_table_launch(int n_pos, double base, float* table, hipStream_t stream);
 // Picks the prefill variant (fills the tiling fields of `a`) and launches it on `stream`.
@@ -90,6 +104,8 @@ hipError_t backward_launch(bool bf16, BackwardArgs a, hipStream_t stream);
 // Workspace bytes of the backward pass: D, then (256-byte aligned) the sink partials.
 size_t backward_ws_d_bytes(int B, int L, int Hq);
 size_t backward_ws_bytes(int B, int L, int Hq);
+// Commits the accepted new tokens of every sequence into its cache on `stream`.
+hipError_t cache_append_launch(bool bf16, const AppendArgs& a, hipStream_t stream);
 // Workspace bytes for nsplit > 1 partial records (0 otherwise).
 size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit);
 

@@ -105,8 +105,7 @@ def decode(lib, dt=BF16, B=4, T=4, Hq=64, Hkv=8, dqk=192, dv=128, q=P, kn=P, vn=
 
 @pytest.mark.parametrize("kw,code", [
     (dict(T=0), EINVAL),
-    (dict(T=5), EINVAL),
-    (dict(Hq=64, Hkv=1, T=4), EUNSUPPORTED),  # 256 query columns per KV head
+    (dict(T=9), EINVAL),                      # at most 8 new tokens (block drafts of 6 or 8)
     (dict(C=126), EINVAL),                    # ring too small for W = 128
     (dict(C=0), EINVAL),
     (dict(max_len=-1), EINVAL),
@@ -142,7 +141,7 @@ def test_workspace_size_query(lib):
     assert mimo.decode_workspace_size(8, 4, 64, 4, 128, 262144, 1 << 30) == 8 * 4 * 32 * 64 * 132 * 4
     assert mimo.decode_workspace_size(8, 4, 64, 4, 128, 262144, 1 << 30, 7) == 8 * 4 * 7 * 64 * 132 * 4
     # invalid arguments -> 0
-    assert mimo.decode_workspace_size(8, 5, 64, 4, 128, 1000, 128) == 0
+    assert mimo.decode_workspace_size(8, 9, 64, 4, 128, 1000, 128) == 0
     assert mimo.decode_workspace_size(8, 4, 64, 4, 96, 1000, 128) == 0
 
 
@@ -200,7 +199,7 @@ def decode_rope(lib, table=P, positions=1004, rot=64, max_len=1000, T=4):
     (dict(table=None), EINVAL),
     (dict(positions=1003), EINVAL),        # needs max_len + T rows
     (dict(rot=0), EUNSUPPORTED),
-    (dict(T=5, positions=2000), EINVAL),   # the plain decode checks still apply
+    (dict(T=9, positions=2000), EINVAL),   # the plain decode checks still apply
 ])
 def test_decode_rope_validation(lib, kw, code):
     assert decode_rope(lib, **kw) == code
@@ -248,3 +247,31 @@ def test_backward_workspace_size(lib):
     assert backward(lib, Hq=4, Hkv=2, ws_bytes=n - 1, kvm=bad_map) == EWORKSPACE
     assert backward(lib, Hq=4, Hkv=2, ws_bytes=n, kvm=bad_map) == EINVAL
     assert "KV head" in mimo.last_error()
+
+
+# ------------------------------------------------------------------------------- cache commit
+
+def append(lib, dt=BF16, B=2, T=4, Hkv=8, dqk=192, dv=128, kn=P, vn=P, kc=P, vc=P, C=128, lens=P,
+           offs=None, acc=None, max_len=1000):
+    return lib.mimo_attn_cache_append(dt, B, T, Hkv, dqk, dv, kn, vn, kc, vc, C, lens, offs, acc,
+                                      max_len, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), EUNSUPPORTED),
+    (dict(B=0), EINVAL),
+    (dict(T=0), EINVAL),
+    (dict(T=9), EINVAL),
+    (dict(Hkv=0), EINVAL),
+    (dict(dv=192), EUNSUPPORTED),
+    (dict(C=0), EINVAL),
+    (dict(max_len=-1), EINVAL),
+    (dict(lens=None), EINVAL),
+    (dict(kc=None), EINVAL),
+    (dict(vn=P_MIS), EINVAL),
+    (dict(acc=ctypes.c_void_p(0x10002)), EINVAL),
+    (dict(offs=ctypes.c_void_p(0x10001)), EINVAL),
+])
+def test_cache_append_validation(lib, kw, code):
+    assert append(lib, **kw) == code
+    assert mimo.last_error() != ""
