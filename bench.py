@@ -14,7 +14,9 @@ timed steps. One JSON line goes to stdout, with:
   workload (a reported baseline, not a target);
 * secondary - the other measured workloads (fp32 prefill, global prefill, ring decode, split-KV
   global decode, both decodes at the 16K-context / 64-sequence MTP setting, the four bf16
-  workloads with the rotary embedding fused, and the backward pass of both bf16 prefills),
+  workloads with the rotary embedding fused, both decodes with 8-token block drafts, the commit
+  of 8 accepted tokens into the sliding-window rings, and the backward pass of both bf16
+  prefills),
   timed the same way, with decode inputs rotated over enough copies to defeat the 256 MiB MALL.
 """
 
@@ -209,6 +211,38 @@ class Case:
                 "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref))}
 
 
+def time_cache_append(steps=50):
+    """Commit of 8 accepted tokens per sequence into the 128-slot rings of the sliding-window
+    decode workload (256 sequences, 8 KV heads): HIP-event time per call and the bytes it moves
+    (each K/V row read once from the new-token tensors and written once into the ring)."""
+    import torch
+
+    import sliding_window_sink_seeded_amd as mimo
+    from sliding_window_sink_seeded_amd import inputs, workloads
+
+    w = workloads.WORKLOADS["swa_decode_t8_bf16"]
+    inp = inputs.decode_inputs(w.seed, w.B, w.T, w.Hq, w.Hkv, w.dqk, w.dv, w.C, w.window, w.dtype,
+                               len_range=w.len_range, ring_offsets=True)
+    up = lambda x: inputs.to_torch(x, w.dtype)
+    kn, vn, kc, vc = up(inp.k_new), up(inp.v_new), up(inp.k_cache), up(inp.v_cache)
+    lens = torch.from_numpy(inp.cache_len).cuda()
+    offs = torch.from_numpy(inp.cache_offset).cuda()
+    for _ in range(5):  # the rings keep wrapping: every call is a full commit
+        mimo.cache_append(kn, vn, kc, vc, lens, (1 << 30) - 8, cache_offset=offs)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        mimo.cache_append(kn, vn, kc, vc, lens, (1 << 30) - 8, cache_offset=offs)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    nbytes = 2 * w.B * w.T * w.Hkv * (w.dqk + w.dv) * w.elem
+    return {"workload": "swa_cache_append_t8_bf16", "kernel_ms": round(ms, 4),
+            "algorithmic_bytes": nbytes, "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "description": "commit of 8 accepted tokens x 256 sequences x 8 KV heads into 128-slot rings"}
+
+
 def _pad_q(rq, n_before):
     """Place one query row at slice position n_before (earlier rows are never read)."""
     import numpy as np
@@ -388,7 +422,8 @@ def main():
         for name in ("swa_prefill_f32", "ga_prefill_bf16", "swa_decode_bf16", "ga_decode_bf16",
                      "swa_decode_mtp_bf16", "ga_decode_mtp_bf16", "swa_prefill_rope_bf16",
                      "ga_prefill_rope_bf16", "swa_decode_rope_bf16", "ga_decode_rope_bf16",
-                     "swa_backward_bf16", "ga_backward_bf16"):
+                     "swa_decode_t8_bf16", "ga_decode_t8_bf16", "swa_backward_bf16",
+                     "ga_backward_bf16"):
             if name == w.name:
                 continue
             c = Case(workloads.WORKLOADS[name])
@@ -398,6 +433,11 @@ def main():
             secondary.append(d)
             del c
             torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        d = time_cache_append()
+        log(f"[bench] cache append: {d}")
+        secondary.append(d)
 
     tflops = head["algorithmic_flop"] / (wall_ms * 1e-3) / 1e12
     line = {

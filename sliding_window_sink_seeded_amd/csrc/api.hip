@@ -334,6 +334,8 @@ int decode_impl(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
   a.nsplit = plan.nsplit;
   a.keys_per_split = plan.keys_per_split;
   a.ncols = a.G * T;
+  // more than kMaxCols query columns per KV head (e.g. 16 heads x 8 tokens) are cut into chunks
+  // that run as separate workgroups
   a.n_chunks = (a.ncols + mimo::kMaxCols - 1) / mimo::kMaxCols;
   if ((long long)a.Hkv * a.n_chunks > 65535) return fail(MIMO_EUNSUPPORTED, "too many KV heads x column chunks");
   if (int rc = group_heads(Hq, Hkv, kv_head_of_q, &a.hl)) return rc;

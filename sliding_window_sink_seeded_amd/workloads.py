@@ -82,6 +82,15 @@ WORKLOADS = {
         description="global decode bf16, 64 seqs x 16384 cached + 4 tokens, 64/4 heads, split-KV"),
 }
 
+# Block-draft verification (MiMo series notes (plmsmile), MiMo-V2.6 decoding ablation: DFlash
+# blocks of 6 and 8 tokens): the two bf16 decode workloads with 8 new tokens per sequence.
+for _name in ("swa_decode_bf16", "ga_decode_bf16"):
+    _w = WORKLOADS[_name]
+    _tn = _name.replace("_bf16", "_t8_bf16")
+    WORKLOADS[_tn] = Workload(**{**_w.__dict__, "name": _tn, "T": 8,
+                                 "description": _w.description.replace("x 4 tokens", "x 8 tokens")
+                                 .replace("+ 4 tokens", "+ 8 tokens") + " (block draft of 8)"})
+
 # The training backward pass of the two bf16 prefill workloads (MiMo-V2-Flash Technical Report
 # review (xllm-io), §3.2: the sink logit is learned, so its gradient is computed too).
 WORKLOADS["swa_backward_bf16"] = Workload(
