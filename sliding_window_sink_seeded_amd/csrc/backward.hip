@@ -190,6 +190,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
 
 // ---------------------------------------------------------------------------------- dK/dV kernel
 
+#ifndef MIMO_DKDV_SGB
+#define MIMO_DKDV_SGB 6
+#endif
+#ifndef MIMO_DKDV_ORDER
+#define MIMO_DKDV_ORDER 1
+#endif
+
 // LDS stage of one step: Q rows [32][kQS], dO rows [32][kOS], then lse * log2(e) [32] and D [32].
 // Row strides are padded so that both the 16-byte row reads and the transposing reads of the MFMA
 // operands spread over the banks.
@@ -246,6 +253,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   const int qt0 = kb0 / kQT;
   const int ntiles = last_q / kQT - qt0 + 1;
   const int nsteps = a.G * ntiles;
+  // Step order: tile-major from the last query tile down, every head of a tile in turn. All
+  // workgroups start at the last tile of the sequence, so the ones running together read the
+  // same Q / dO rows at about the same time and share them through L2 (head-major order made
+  // each workgroup walk its own tiles and re-read Q / dO from HBM).
+#if MIMO_DKDV_ORDER
+  const int qt_last = last_q / kQT;
+  auto step_head = [&](int step) { return step % a.G; };
+  auto step_row = [&](int step) { return (qt_last - step / a.G) * kQT; };
+#else
+  auto step_head = [&](int step) { return step / ntiles; };
+  auto step_row = [&](int step) { return (qt0 + step % ntiles) * kQT; };
+#endif
 
   // staging: thread tid moves row tid / 8 of the step's Q and dO tiles; threads 0..63 also move
   // lse (rows 0..31) and D (rows 32..63 -> D of row tid - 32)
@@ -255,8 +274,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   u32x4 qr[QPT], orr[OPT];
   float lr = 0.f;
   auto load_step = [&](int step) {
-    const int j = step / ntiles;
-    const int q0 = (qt0 + step % ntiles) * kQT;
+    const int j = step_head(step);
+    const int q0 = step_row(step);
     const int head = a.hl.at(g * a.G + j);
     const int qrow = min(q0 + srow, a.L - 1);
     const char* qp = (const char*)a.q + ((size_t)b * a.L + qrow) * qrow_stride + (size_t)head * kDQK * E::kBytes;
@@ -289,25 +308,54 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   wait_all();
   __syncthreads();
 
+  f32x16 acck[kDQK / 32], accv[kDV / 32];
+  // Operand reads go through one per-lane base pointer per step plus compile-time offsets, which
+  // become the LDS instructions' immediate offsets (written as lane offset + constant, the
+  // compiler kept one hoisted address per read and added the stage to each of them every step).
+  const int row_lane = (col * St::kQS + 8 * half) * E::kBytes;                     // Q row reads
+  const int orow_lane = St::kQBytes + (col * St::kOS + 8 * half) * E::kBytes;      // dO row reads
+  const int tr_row = 4 * half + ((lane & 15) >> 2), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int qtr_lane = (tr_row * St::kQS + tr_col) * E::kBytes;                    // Q^T reads
+  const int otr_lane = St::kQBytes + (tr_row * St::kOS + tr_col) * E::kBytes;      // dO^T reads
+  auto row_frag = [&](const char* p) -> Frag {
+    if constexpr (E::kBytes == 2) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+    } else {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+      const f32x4 y = *reinterpret_cast<const f32x4*>(p + 16);
+      Frag f;
+      f[0] = x[0]; f[1] = x[1]; f[2] = x[2]; f[3] = x[3];
+      f[4] = y[0]; f[5] = y[1]; f[6] = y[2]; f[7] = y[3];
+      return f;
+    }
+  };
+  // bf16: rows 16 ks + 4 half + 0..3 and + 8 of columns 32 t + lane % 32, through the
+  // transposing read (see vt_frag_tr); p already holds the lane's part of the address
+  auto tr_frag = [&](const char* p, int stride) -> bf16x8 {
+    const s16x4 x = lds_read_tr16(p);
+    const s16x4 y = lds_read_tr16(p + 8 * stride * 2);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 u;
+    u[0] = x[0]; u[1] = x[1]; u[2] = x[2]; u[3] = x[3];
+    u[4] = y[0]; u[5] = y[1]; u[6] = y[2]; u[7] = y[3];
+    return __builtin_bit_cast(bf16x8, u);
+  };
   // One step: S = Q K^T and dP = dO V^T for the staged (head, query tile), then P, dS and the
   // dV / dK contributions. A wave none of whose keys the tile sees computes with p = 0 (no
   // branch: branches inside the loop make the compiler move the accumulators between register
   // files on every step).
-  f32x16 acck[kDQK / 32], accv[kDV / 32];
   auto compute = [&](int step, bool first) {
-    const int q0 = (qt0 + step % ntiles) * kQT;
+    const int q0 = step_row(step);
     const bool active = (kw0 < a.L) && (q0 + kQT - 1 >= kw0) && (q0 <= kw0 + 31 + a.window - 1);
     const unsigned wlim = active ? (unsigned)a.window : 0u;  // no visible key when inactive
     const char* stage = smem + (step & 1) * St::kBytes;
-    const char* sq = stage;
-    const char* so = stage + St::kQBytes;
     const float* sl = reinterpret_cast<const float*>(stage + St::kQBytes + St::kOBytes);
 
     f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-    for (int kk = 0; kk < kDQK / 16; ++kk) s = mma(lds_row_frag<E>(sq, St::kQS, col, kk, half), kf[kk], s);
+    for (int kk = 0; kk < kDQK / 16; ++kk) s = mma(row_frag(stage + row_lane + 16 * kk * E::kBytes), kf[kk], s);
 #pragma unroll
-    for (int kk = 0; kk < kDV / 16; ++kk) dp = mma(lds_row_frag<E>(so, St::kOS, col, kk, half), vf[kk], dp);
+    for (int kk = 0; kk < kDV / 16; ++kk) dp = mma(row_frag(stage + orow_lane + 16 * kk * E::kBytes), vf[kk], dp);
 
     // register r holds query row 8 (r / 4) + 4 half + r % 4 of the tile
 #pragma unroll
@@ -329,13 +377,44 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
     for (int ks = 0; ks < kQT / 16; ++ks) {
       const Frag pf = frag_from_acc<E>(s, 8 * ks);
 #pragma unroll
-      for (int t = 0; t < kDV / 32; ++t)
-        accv[t] = mma(lds_t_frag<E>(so, St::kOS, t, ks, lane), pf, (first && ks == 0) ? zero16() : accv[t]);
+      for (int t = 0; t < kDV / 32; ++t) {
+        Frag f;
+        if constexpr (E::kBytes == 2)
+          f = tr_frag(stage + otr_lane + (16 * ks * St::kOS + 32 * t) * 2, St::kOS);
+        else
+          f = lds_t_frag<E>(stage + St::kQBytes, St::kOS, t, ks, lane);
+        accv[t] = mma(f, pf, (first && ks == 0) ? zero16() : accv[t]);
+      }
       const Frag dsf = frag_from_acc<E>(dp, 8 * ks);
 #pragma unroll
-      for (int t = 0; t < kDQK / 32; ++t)
-        acck[t] = mma(lds_t_frag<E>(sq, St::kQS, t, ks, lane), dsf, (first && ks == 0) ? zero16() : acck[t]);
+      for (int t = 0; t < kDQK / 32; ++t) {
+        Frag f;
+        if constexpr (E::kBytes == 2)
+          f = tr_frag(stage + qtr_lane + (16 * ks * St::kQS + 32 * t) * 2, St::kQS);
+        else
+          f = lds_t_frag<E>(stage, St::kQS, t, ks, lane);
+        acck[t] = mma(f, dsf, (first && ks == 0) ? zero16() : acck[t]);
+      }
     }
+#if MIMO_DKDV_SGB
+    // Issue order: LDS operand reads run several MFMAs ahead (one wave per SIMD cannot hide an
+    // LDS round trip behind another wave). Phase 1: 20 row reads for 20 MFMAs; phase 2: 40
+    // transposing reads (two per fragment) for 20 MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, MIMO_DKDV_SGB, 0);
+#pragma unroll
+    for (int i = 0; i < 20 - MIMO_DKDV_SGB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MIMO_DKDV_SGB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MIMO_DKDV_SGB, 0);
+#pragma unroll
+    for (int i = 0; i < 20 - MIMO_DKDV_SGB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MIMO_DKDV_SGB, 0);
+#endif
   };
 
   // Step 0 is peeled so that the accumulators start as MFMA results. The scheduling barriers
