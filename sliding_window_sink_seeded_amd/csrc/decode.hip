@@ -132,8 +132,8 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
   const int g = blockIdx.y / a.n_chunks;
   const int b = blockIdx.z;
   // this workgroup's query columns: cbase + [0, ncols) of the G*T columns of (b, g)
-  const int cbase = chunk * kMaxCols;
-  const int ncols = min(kMaxCols, a.ncols - cbase);
+  const int cbase = chunk * a.chunk_cols;
+  const int ncols = min(a.chunk_cols, a.ncols - cbase);
 
   int P = a.cache_len[b];
   P = P < 0 ? 0 : (P > a.max_len ? a.max_len : P);
@@ -667,7 +667,7 @@ template <bool ROPE>
 static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.nsplit, a.Hkv * a.n_chunks, a.B);
   const dim3 block(kDecNW * 64);
-  const bool two = (a.n_chunks > 1 ? kMaxCols : a.ncols) > 32;
+  const bool two = (a.n_chunks > 1 ? a.chunk_cols : a.ncols) > 32;
   if (bf16 && two)
     hipLaunchKernelGGL((decode_kernel<BF16, 2, true, ROPE>), grid, block, 0, stream, a);
   else if (bf16)

@@ -48,7 +48,8 @@ struct DecodeArgs {
   int nsplit;
   int keys_per_split;  // multiple of 32
   int ncols;           // G * T query columns per KV head
-  int n_chunks;        // ceil(ncols / kMaxCols) workgroups share them
+  int chunk_cols;      // query columns per workgroup (32 or kMaxCols)
+  int n_chunks;        // ceil(ncols / chunk_cols) workgroups share them
   const float* rope;   // [>= max_len + T][32][2] (cos, sin) when q/k_new arrive unrotated, else NULL
   HeadList hl;
 };
