@@ -271,9 +271,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   const int srow = tid >> 3, spart = tid & 7;
   const size_t qrow_stride = (size_t)a.Hq * kDQK * E::kBytes;
   const size_t orow_stride = (size_t)a.Hq * kDV * E::kBytes;
-  u32x4 qr[QPT], orr[OPT];
-  float lr = 0.f;
-  auto load_step = [&](int step) {
+  struct Staged {
+    u32x4 q[QPT], o[OPT];
+    float l;
+  };
+  auto load_step = [&](int step, Staged& r) {
     const int j = step_head(step);
     const int q0 = step_row(step);
     const int head = a.hl.at(g * a.G + j);
@@ -281,30 +283,31 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
     const char* qp = (const char*)a.q + ((size_t)b * a.L + qrow) * qrow_stride + (size_t)head * kDQK * E::kBytes;
     const char* op = (const char*)a.d_o + ((size_t)b * a.L + qrow) * orow_stride + (size_t)head * kDV * E::kBytes;
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) qr[i] = ld16(qp + 16 * (spart * QPT + i));
+    for (int i = 0; i < QPT; ++i) r.q[i] = ld16(qp + 16 * (spart * QPT + i));
 #pragma unroll
-    for (int i = 0; i < OPT; ++i) orr[i] = ld16(op + 16 * (spart * OPT + i));
+    for (int i = 0; i < OPT; ++i) r.o[i] = ld16(op + 16 * (spart * OPT + i));
     {  // every thread loads (threads past 64 re-read a D entry): no branch and no use of the
        // value before store_step, so nothing waits for this load here
-      const int r = min(q0 + (tid & 31), a.L - 1);
-      const size_t li = ((size_t)b * a.Hq + head) * a.L + r;
-      lr = (tid < kQT ? a.lse : a.D)[li];
+      const int rr = min(q0 + (tid & 31), a.L - 1);
+      const size_t li = ((size_t)b * a.Hq + head) * a.L + rr;
+      r.l = (tid < kQT ? a.lse : a.D)[li];
     }
   };
-  auto store_step = [&](char* stage) {
+  auto store_step = [&](char* stage, const Staged& r) {
     char* sq = stage + (srow * St::kQS + spart * QPT * (16 / E::kBytes)) * E::kBytes;
     char* so = stage + St::kQBytes + (srow * St::kOS + spart * OPT * (16 / E::kBytes)) * E::kBytes;
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) st16(sq + 16 * i, qr[i]);
+    for (int i = 0; i < QPT; ++i) st16(sq + 16 * i, r.q[i]);
 #pragma unroll
-    for (int i = 0; i < OPT; ++i) st16(so + 16 * i, orr[i]);
+    for (int i = 0; i < OPT; ++i) st16(so + 16 * i, r.o[i]);
     if (tid < 2 * kQT)
-      reinterpret_cast<float*>(stage + St::kQBytes + St::kOBytes)[tid] = tid < kQT ? lr * kLog2e : lr;
+      reinterpret_cast<float*>(stage + St::kQBytes + St::kOBytes)[tid] = tid < kQT ? r.l * kLog2e : r.l;
   };
 
   const float c = a.scale_log2;
-  load_step(0);
-  store_step(smem);
+  Staged ra;
+  load_step(0, ra);
+  store_step(smem, ra);
   wait_all();
   __syncthreads();
 
@@ -420,18 +423,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   // Step 0 is peeled so that the accumulators start as MFMA results. The scheduling barriers
   // keep the next step's loads ahead of the math and its LDS stores behind it (left alone, the
   // scheduler pulls the stores up next to the loads and every step waits for global memory).
-  load_step(min(1, nsteps - 1));
+  auto stage = [&](int step) { return smem + (step & 1) * St::kBytes; };
+  load_step(min(1, nsteps - 1), ra);
   __builtin_amdgcn_sched_barrier(0);
   compute(0, true);
   __builtin_amdgcn_sched_barrier(0);
-  store_step(smem + St::kBytes);
+  store_step(stage(1), ra);
   __syncthreads();
   for (int step = 1; step < nsteps; ++step) {
-    load_step(min(step + 1, nsteps - 1));
+    load_step(min(step + 1, nsteps - 1), ra);
     __builtin_amdgcn_sched_barrier(0);
     compute(step, false);
     __builtin_amdgcn_sched_barrier(0);
-    store_step(smem + ((step + 1) & 1) * St::kBytes);
+    store_step(stage(step + 1), ra);
     __syncthreads();
   }
 
