@@ -51,9 +51,11 @@ struct DecodeLds {
   static constexpr int kVBytes = (kVRowMajor ? 32 : kDDV) * kVStride * E::kBytes;
   static constexpr int kMergeBytes = kDecNW * 2 * 16 * 64 * 4;  // two dv blocks of one column block
   static constexpr int kWorkBytes = kDecNW * kVBytes > kMergeBytes ? kDecNW * kVBytes : kMergeBytes;
-  // new-token K and V rows (T <= kMaxNew), staged with Q at kernel start
-  static constexpr int kNewKBytes = kMaxNew * kDDQK * E::kBytes;
-  static constexpr int kNewBytes = kNewKBytes + kMaxNew * kDDV * E::kBytes;
+  // K and V rows of new tokens 0..3, staged with Q at kernel start (tokens 4..7 of a block draft
+  // go to the work area after the key loop, which keeps the ring kernel at three workgroups per CU)
+  static constexpr int kNewKBytes = 4 * kDDQK * E::kBytes;
+  static constexpr int kNewBytes = kNewKBytes + 4 * kDDV * E::kBytes;
+  static_assert(4 * (kDDQK + kDDV) * E::kBytes <= kDecNW * kVBytes, "tokens 4..7 fit the V tiles");
   static constexpr int kBytes = kQBytes + kNewBytes + kWorkBytes + kDecNW * 64 * 4 * 2;
 };
 
@@ -385,19 +387,20 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
     }
   }
 
-  // ---- block drafts (T > 4, last split): new tokens 4 .. T-1 are staged only now, when the
-  // registers of the key loop are free (staging them with the first four costs the whole kernel
-  // some 50 registers) ----
+  // ---- block drafts (T > 4, last split): new tokens 4 .. T-1 are staged only now, into the V
+  // tiles of the work area (idle until the merge), when the registers of the key loop are free
+  // (staging them with the first four costs the whole kernel some 50 registers) ----
+  char* snew_hi = work;  // K rows of tokens 4..7, then their V rows
   if (split == a.nsplit - 1 && a.T > 4) {
     constexpr int kKCh = kDDQK / E::kPerChunk, kVCh = kDDV / E::kPerChunk;
-    char* snew = smem + Lds::kQBytes;
+    __syncthreads();  // every wave is done with its V tile
     for (int u = tid; u < (a.T - 4) * (kKCh + kVCh); u += kDecNW * 64) {
       const int t = 4 + u / (kKCh + kVCh), ch = u % (kKCh + kVCh);
       if (ch < kKCh)
-        st16(snew + t * kDDQK * E::kBytes + ch * 16,
+        st16(snew_hi + (t - 4) * kDDQK * E::kBytes + ch * 16,
              ld16((const char*)a.k_new + (((size_t)b * a.T + t) * a.Hkv + g) * krow_bytes + ch * 16));
       else
-        st16(snew + Lds::kNewKBytes + t * kDDV * E::kBytes + (ch - kKCh) * 16,
+        st16(snew_hi + Lds::kNewKBytes + (t - 4) * kDDV * E::kBytes + (ch - kKCh) * 16,
              ld16((const char*)a.v_new + (((size_t)b * a.T + t) * a.Hkv + g) * vrow_bytes + (ch - kKCh) * 16));
     }
     __syncthreads();
@@ -405,8 +408,10 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
 
   // ---- new tokens wave, wave + 4 (last split only): one extra key per column, on the VALU ----
   for (int tn = wave; split == a.nsplit - 1 && tn < a.T; tn += kDecNW) {
-    const char* krow = smem + Lds::kQBytes + tn * kDDQK * E::kBytes;  // staged in LDS
-    const char* vrow = smem + Lds::kQBytes + Lds::kNewKBytes + tn * kDDV * E::kBytes;
+    // staged in LDS: tokens 0..3 next to Q, tokens 4..7 in the work area
+    const char* nbase = tn < 4 ? smem + Lds::kQBytes : snew_hi;
+    const char* krow = nbase + (tn & 3) * kDDQK * E::kBytes;
+    const char* vrow = nbase + Lds::kNewKBytes + (tn & 3) * kDDV * E::kBytes;
     const float c = a.scale_log2;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
