@@ -437,6 +437,10 @@ static hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+#ifndef MIMO_F32_NW4
+#define MIMO_F32_NW4 1
+#endif
+
 #ifndef MIMO_SWA_WG_PER_CU
 #define MIMO_SWA_WG_PER_CU 4
 #endif
@@ -494,7 +498,21 @@ hipError_t prefill_launch(bool bf16, PrefillArgs a, hipStream_t stream) {
   const int rows_per_wg = kQT * (NW / hg);
   a.n_qblocks = (a.L + rows_per_wg - 1) / rows_per_wg;
   const bool global = a.window >= a.L;
-  if (!bf16) return launch<F32, NW, 32>(a, stream);
+  if (!bf16) {
+    // fp32 (the small configurations): four-wave workgroups when eight-wave ones would leave
+    // compute units idle (1 x 512 rows x 8 KV heads: 128 workgroups of eight waves)
+    if (MIMO_F32_NW4 && (long long)a.n_qblocks * a.B * a.Hkv * a.n_hchunks < 2 * 256) {
+      constexpr int NW4 = 4;
+      int hg4 = 1;
+      while (hg4 < NW4 && a.G % (hg4 * 2) == 0) hg4 *= 2;
+      a.heads_per_wg = hg4;
+      a.n_hchunks = a.G / hg4;
+      const int rows4 = kQT * (NW4 / hg4);
+      a.n_qblocks = (a.L + rows4 - 1) / rows4;
+      return launch<F32, NW4, 32>(a, stream);
+    }
+    return launch<F32, NW, 32>(a, stream);
+  }
   if (!global && hg == NW && a.window <= 129) {
     const int nb = (a.window - 1 + 31) / 32 + 1;  // 32-key blocks in a 32-row tile's window
     switch (nb) {
