@@ -193,9 +193,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
 #ifndef MIMO_DKDV_SGB
 #define MIMO_DKDV_SGB 6
 #endif
-#ifndef MIMO_DKDV_ORDER
-#define MIMO_DKDV_ORDER 1
-#endif
 
 // LDS stage of one step: Q rows [32][kQS], dO rows [32][kOS], then lse * log2(e) [32] and D [32].
 // Row strides are padded so that both the 16-byte row reads and the transposing reads of the MFMA
@@ -257,14 +254,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   // workgroups start at the last tile of the sequence, so the ones running together read the
   // same Q / dO rows at about the same time and share them through L2 (head-major order made
   // each workgroup walk its own tiles and re-read Q / dO from HBM).
-#if MIMO_DKDV_ORDER
   const int qt_last = last_q / kQT;
   auto step_head = [&](int step) { return step % a.G; };
   auto step_row = [&](int step) { return (qt_last - step / a.G) * kQT; };
-#else
-  auto step_head = [&](int step) { return step / ntiles; };
-  auto step_row = [&](int step) { return (qt0 + step % ntiles) * kQT; };
-#endif
 
   // staging: thread tid moves row tid / 8 of the step's Q and dO tiles; threads 0..63 also move
   // lse (rows 0..31) and D (rows 32..63 -> D of row tid - 32)

@@ -32,9 +32,6 @@ namespace mimo {
 // ------------------------------------------------------------------------ generic streaming kernel
 
 constexpr float kLazyRescale = 8.f;  // log2 units
-#ifndef MIMO_SETPRIO
-#define MIMO_SETPRIO 0
-#endif
 
 template <typename E, int NW, int BK, bool ROPE>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
@@ -121,13 +118,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
       f32x16 s[NSB];
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) s[sb] = zero16();
-      if (MIMO_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < kDQK / 16; ++kk)
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb)
           s[sb] = mma(lds_k_frag<E, BK>(sk, 32 * sb + col, kk, half), qf[kk], s[sb]);
-      if (MIMO_SETPRIO) __builtin_amdgcn_s_setprio(0);
 
       float bmax = -INFINITY;
 #pragma unroll
@@ -168,8 +163,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
         }
       }
       l += halves_sum(rs);
-
-      if (MIMO_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
         const Frag pf = frag_from_acc<E>(s[ks >> 1], 8 * (ks & 1));
@@ -177,7 +170,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
         for (int db = 0; db < kDV / 32; ++db)
           acc[db] = mma(lds_vt_frag<E, BK>(sv, db, ks, lane), pf, acc[db]);
       }
-      if (MIMO_SETPRIO) __builtin_amdgcn_s_setprio(0);
     }
 
     if (ib + 1 < nblk) st.store(smem + ((ib + 1) & 1) * Tile::kStageBytes, tid);
@@ -437,10 +429,6 @@ static hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-#ifndef MIMO_F32_NW4
-#define MIMO_F32_NW4 1
-#endif
-
 #ifndef MIMO_SWA_WG_PER_CU
 #define MIMO_SWA_WG_PER_CU 4
 #endif
@@ -501,7 +489,7 @@ hipError_t prefill_launch(bool bf16, PrefillArgs a, hipStream_t stream) {
   if (!bf16) {
     // fp32 (the small configurations): four-wave workgroups when eight-wave ones would leave
     // compute units idle (1 x 512 rows x 8 KV heads: 128 workgroups of eight waves)
-    if (MIMO_F32_NW4 && (long long)a.n_qblocks * a.B * a.Hkv * a.n_hchunks < 2 * 256) {
+    if ((long long)a.n_qblocks * a.B * a.Hkv * a.n_hchunks < 2 * 256) {
       constexpr int NW4 = 4;
       int hg4 = 1;
       while (hg4 < NW4 && a.G % (hg4 * 2) == 0) hg4 *= 2;
