@@ -339,7 +339,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   // dV / dK contributions. A wave none of whose keys the tile sees computes with p = 0 (no
   // branch: branches inside the loop make the compiler move the accumulators between register
   // files on every step).
-  auto compute = [&](int step, bool first) {
+  auto compute = [&](int step, bool first, auto masked) {
     const int q0 = step_row(step);
     const bool active = (kw0 < a.L) && (q0 + kQT - 1 >= kw0) && (q0 <= kw0 + 31 + a.window - 1);
     const unsigned wlim = active ? (unsigned)a.window : 0u;  // no visible key when inactive
@@ -361,9 +361,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * gq + i;
         const int qp = q0 + 8 * gq + 4 * half + i;
-        const bool vis = (unsigned)(qp - kpos) < wlim && qp < a.L;
-        // select the exponent, not the result: exp2(-inf) = 0 needs no branch
-        const float p = fast_exp2(vis ? __builtin_fmaf(s[r], c, -l4[i]) : -INFINITY);
+        float p;
+        if constexpr (decltype(masked)::value) {
+          const bool vis = (unsigned)(qp - kpos) < wlim && qp < a.L;
+          // select the exponent, not the result: exp2(-inf) = 0 needs no branch
+          p = fast_exp2(vis ? __builtin_fmaf(s[r], c, -l4[i]) : -INFINITY);
+        } else {
+          p = fast_exp2(__builtin_fmaf(s[r], c, -l4[i]));
+        }
         s[r] = p;
         dp[r] = p * (dp[r] - d4[i]);
       }
@@ -415,21 +420,48 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   // Step 0 is peeled so that the accumulators start as MFMA results. The scheduling barriers
   // keep the next step's loads ahead of the math and its LDS stores behind it (left alone, the
   // scheduler pulls the stores up next to the loads and every step waits for global memory).
+  //
+  // Steps whose tile every key of the workgroup sees in full need no mask: rows at or after the
+  // block's last key (q0 >= kb0 + 32 NW - 1), inside the window of its first key, and before L.
+  // In the descending order they form one run [s_a, s_b); the steps before (a partial last tile)
+  // and after it (the tiles on the diagonal) take the masked variant. Each loop stays free of
+  // branches.
   auto stage = [&](int step) { return smem + (step & 1) * St::kBytes; };
+  int s_a = 0, s_b = 0;
+  {
+    // tile t is interior iff 32 t >= kb0 + 32 NW - 1, 32 t <= kb0 + W - 32 and 32 t <= L - 32
+    const int t_lo = (kb0 + 32 * NW - 1 + kQT - 1) / kQT;
+    const long long lim = min((long long)kb0 + a.window - kQT, (long long)a.L - kQT);
+    if (lim >= 0) {
+      const int t_hi = (int)min((long long)qt_last, lim / kQT);
+      if (t_lo <= t_hi) {
+        s_a = (qt_last - t_hi) * a.G;
+        s_b = (qt_last - t_lo + 1) * a.G;
+      }
+    }
+  }
+  auto run = [&](int s0, int s1, auto masked) {
+    for (int step = s0; step < s1; ++step) {
+      load_step(min(step + 1, nsteps - 1), ra);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(step, false, masked);
+      __builtin_amdgcn_sched_barrier(0);
+      store_step(stage(step + 1), ra);
+      __syncthreads();
+    }
+  };
   load_step(min(1, nsteps - 1), ra);
   __builtin_amdgcn_sched_barrier(0);
-  compute(0, true);
+  if (s_a == 0 && s_b > 0)
+    compute(0, true, BoolTag<false>{});
+  else
+    compute(0, true, BoolTag<true>{});
   __builtin_amdgcn_sched_barrier(0);
   store_step(stage(1), ra);
   __syncthreads();
-  for (int step = 1; step < nsteps; ++step) {
-    load_step(min(step + 1, nsteps - 1), ra);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(step, false);
-    __builtin_amdgcn_sched_barrier(0);
-    store_step(stage(step + 1), ra);
-    __syncthreads();
-  }
+  run(1, s_a, BoolTag<true>{});
+  run(max(1, s_a), s_b, BoolTag<false>{});
+  run(max(1, s_b), nsteps, BoolTag<true>{});
 
   const bool kvalid = kpos < a.L;
   char* dkrow = (char*)a.dk + krow * kDQK * E::kBytes;
