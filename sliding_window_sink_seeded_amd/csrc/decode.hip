@@ -113,6 +113,106 @@ struct KeyRows {
   }
 };
 
+// Staging of Q^T (one row per query column: head j of the group x new token t, column c = j * T + t,
+// padded columns zero) and of the K/V rows of new tokens 0..3 (tokens 4..7 of a block draft are
+// staged later by the caller). load() issues every global load of the thread, store() writes them
+// to LDS; a caller issues its first K/V block fetch in between. A non-default head map is read
+// before any other load, so that waiting for it waits for nothing else.
+template <typename E, int NCB>
+struct QStage {
+  using Lds = DecodeLds<E, NCB>;
+  static constexpr int kChunksRow = kDDQK / E::kPerChunk;
+  static constexpr int kQChunks = NCB * 32 * kChunksRow;
+  static constexpr int kQPer = (kQChunks + kDecNW * 64 - 1) / (kDecNW * 64);
+  static constexpr int kKCh = kDDQK / E::kPerChunk, kVCh = kDDV / E::kPerChunk;
+  static constexpr int kNewPer = (4 * (kKCh + kVCh) + kDecNW * 64 - 1) / (kDecNW * 64);
+  u32x4 xq[kQPer], xn[kNewPer];
+
+  __device__ __forceinline__ void load(const DecodeArgs& a, int tid, int b, int g, int cbase, int ncols) {
+    const size_t krow_bytes = (size_t)kDDQK * E::kBytes, vrow_bytes = (size_t)kDDV * E::kBytes;
+    int head[kQPer];
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) {
+      const int c = cbase + min((tid + i * kDecNW * 64) / kChunksRow, ncols - 1);  // padding: any valid row
+      head[i] = g * a.G + c / a.T;
+    }
+    if (!a.hl.identity) {
+#pragma unroll
+      for (int i = 0; i < kQPer; ++i) head[i] = a.hl.heads[head[i]];
+    }
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) {
+      const int u = tid + i * kDecNW * 64;
+      const int c = cbase + min(u / kChunksRow, ncols - 1), ch = u % kChunksRow;
+      xq[i] = ld16((const char*)a.q + (((size_t)b * a.T + c % a.T) * a.Hq + head[i]) * krow_bytes + ch * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kNewPer; ++i) {
+      const int u = tid + i * kDecNW * 64;
+      const int t = min(u / (kKCh + kVCh), a.T - 1), ch = u % (kKCh + kVCh);
+      const char* src = ch < kKCh
+                            ? (const char*)a.k_new + (((size_t)b * a.T + t) * a.Hkv + g) * krow_bytes + ch * 16
+                            : (const char*)a.v_new + (((size_t)b * a.T + t) * a.Hkv + g) * vrow_bytes +
+                                  (ch - kKCh) * 16;
+      xn[i] = ld16(src);
+    }
+  }
+
+  // Q^T rows at smem, new tokens 0..3 (K rows, then V rows) right after them; the new tokens only
+  // when `last` (the split that folds them in)
+  __device__ __forceinline__ void store(char* smem, int tid, int ncols, bool last, int T) const {
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) {
+      const int u = tid + i * kDecNW * 64;
+      const int c = u / kChunksRow, ch = u % kChunksRow;
+      if (u < kQChunks) st16(smem + c * Lds::kQStride * E::kBytes + ch * 16, c < ncols ? xq[i] : zero_chunk());
+    }
+    char* snew = smem + Lds::kQBytes;
+#pragma unroll
+    for (int i = 0; i < kNewPer; ++i) {
+      const int u = tid + i * kDecNW * 64;
+      const int t = u / (kKCh + kVCh), ch = u % (kKCh + kVCh);
+      if (last && u < 4 * (kKCh + kVCh) && t < T) {
+        if (ch < kKCh)
+          st16(snew + t * kDDQK * E::kBytes + ch * 16, xn[i]);
+        else
+          st16(snew + Lds::kNewKBytes + t * kDDV * E::kBytes + (ch - kKCh) * 16, xn[i]);
+      }
+    }
+  }
+};
+
+// q and k_new arrive before the rotary embedding: rotate the staged Q^T rows and (last split) the
+// staged new-token K rows in LDS, query column c (token c % T) and new token t at positions
+// P + c % T and P + t; pairs (i, i + 32), i < 32. The caller synchronises before and after.
+template <typename E, int NCB>
+__device__ __forceinline__ void rope_staged(const DecodeArgs& a, char* smem, int tid, int P, int cbase,
+                                            int ncols, bool last) {
+  using Lds = DecodeLds<E, NCB>;
+  constexpr int kHalfRot = kRopeDims / 2;
+  const int n_q = ncols * kHalfRot, n_k = last ? a.T * kHalfRot : 0;
+  for (int u = tid; u < n_q + n_k; u += kDecNW * 64) {
+    const bool is_q = u < n_q;
+    const int uu = is_q ? u : u - n_q;
+    const int row = uu / kHalfRot, i = uu % kHalfRot;
+    const int pos = P + (is_q ? (cbase + row) % a.T : row);
+    char* base = is_q ? smem + row * Lds::kQStride * E::kBytes : smem + Lds::kQBytes + row * kDDQK * E::kBytes;
+    const f32x2 csn = *reinterpret_cast<const f32x2*>(a.rope + ((size_t)pos * kHalfRot + i) * 2);
+    if constexpr (E::kBytes == 2) {
+      uint16_t* e = reinterpret_cast<uint16_t*>(base);
+      const float x = __uint_as_float((uint32_t)e[i] << 16), y = __uint_as_float((uint32_t)e[i + kHalfRot] << 16);
+      e[i] = (uint16_t)bf16_bits(x * csn[0] - y * csn[1]);
+      e[i + kHalfRot] = (uint16_t)bf16_bits(y * csn[0] + x * csn[1]);
+    } else {
+      float* e = reinterpret_cast<float*>(base);
+      const float x = e[i], y = e[i + kHalfRot];
+      e[i] = x * csn[0] - y * csn[1];
+      e[i + kHalfRot] = y * csn[0] + x * csn[1];
+    }
+  }
+}
+
+
 // With one bf16 column block, asking for two waves per SIMD makes the compiler keep the
 // accumulators in VGPRs (169 registers, no AGPR copies) instead of 137 VGPRs + 80 AGPRs; both give
 // two waves per SIMD, the first runs faster (ring workload).
@@ -166,73 +266,19 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
   KeyRows<E> cur;
   int key0 = s0 + 32 * wave;
 
-  // Q^T of every query column (head j of the group x new token t, column c = j * T + t) -> LDS,
-  // and (last split) the new tokens' K/V rows of this (b, g). Every load of a thread is issued
-  // before its first LDS store, and the first K/V block's fetch goes out before those stores so
-  // that its latency overlaps them. A non-default head map is read before any other load, so
-  // that waiting for it waits for nothing else.
+  // Q^T of every query column and (last split) the new tokens' K/V rows of this (b, g) go to LDS;
+  // the first K/V block's fetch is issued between the loads and the LDS stores so that its
+  // latency overlaps them.
   char* sq = smem;
   {
-    constexpr int kChunksRow = kDDQK / E::kPerChunk;
-    constexpr int kQChunks = NCB * 32 * kChunksRow;
-    constexpr int kQPer = (kQChunks + kDecNW * 64 - 1) / (kDecNW * 64);
-    constexpr int kKCh = kDDQK / E::kPerChunk, kVCh = kDDV / E::kPerChunk;
-    // new tokens 0..3 are staged here; 4..7, when present, by a second batch below
-    constexpr int kNewPer = (4 * (kKCh + kVCh) + kDecNW * 64 - 1) / (kDecNW * 64);
-    int head[kQPer];
-#pragma unroll
-    for (int i = 0; i < kQPer; ++i) {
-      const int c = cbase + min((tid + i * kDecNW * 64) / kChunksRow, ncols - 1);  // padding: any valid row
-      head[i] = g * a.G + c / a.T;
-    }
-    if (!a.hl.identity) {
-#pragma unroll
-      for (int i = 0; i < kQPer; ++i) head[i] = a.hl.heads[head[i]];
-    }
-    u32x4 xq[kQPer], xn[kNewPer];
-#pragma unroll
-    for (int i = 0; i < kQPer; ++i) {
-      const int u = tid + i * kDecNW * 64;
-      const int c = cbase + min(u / kChunksRow, ncols - 1), ch = u % kChunksRow;
-      xq[i] = ld16((const char*)a.q + (((size_t)b * a.T + c % a.T) * a.Hq + head[i]) * krow_bytes + ch * 16);
-    }
-    const bool last = split == a.nsplit - 1;
-#pragma unroll
-    for (int i = 0; i < kNewPer; ++i) {
-      const int u = tid + i * kDecNW * 64;
-      const int t = min(u / (kKCh + kVCh), a.T - 1), ch = u % (kKCh + kVCh);
-      const char* src = ch < kKCh
-                            ? (const char*)a.k_new + (((size_t)b * a.T + t) * a.Hkv + g) * krow_bytes + ch * 16
-                            : (const char*)a.v_new + (((size_t)b * a.T + t) * a.Hkv + g) * vrow_bytes +
-                                  (ch - kKCh) * 16;
-      xn[i] = ld16(src);
-    }
+    QStage<E, NCB> st;
+    st.load(a, tid, b, g, cbase, ncols);
     if (key0 < s1) {
       const char *kr, *vr;
       rows(key0, kr, vr);
       cur.load(kr, vr, half);
     }
-#pragma unroll
-    for (int i = 0; i < kQPer; ++i) {
-      const int u = tid + i * kDecNW * 64;
-      const int c = u / kChunksRow, ch = u % kChunksRow;
-      if (u < kQChunks) st16(sq + c * Lds::kQStride * E::kBytes + ch * 16, c < ncols ? xq[i] : zero_chunk());
-    }
-    char* snew = smem + Lds::kQBytes;
-    auto store_new = [&](int t0, const u32x4 (&x)[kNewPer]) {
-#pragma unroll
-      for (int i = 0; i < kNewPer; ++i) {
-        const int u = tid + i * kDecNW * 64;
-        const int t = t0 + u / (kKCh + kVCh), ch = u % (kKCh + kVCh);
-        if (last && u < 4 * (kKCh + kVCh) && t < a.T) {
-          if (ch < kKCh)
-            st16(snew + t * kDDQK * E::kBytes + ch * 16, x[i]);
-          else
-            st16(snew + Lds::kNewKBytes + t * kDDV * E::kBytes + (ch - kKCh) * 16, x[i]);
-        }
-      }
-    };
-    store_new(0, xn);
+    st.store(smem, tid, ncols, split == a.nsplit - 1, a.T);
   }
 
   int qpos[NCB];
@@ -269,30 +315,7 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
   __syncthreads();  // Q^T and the new-token rows are in LDS
 
   if constexpr (ROPE) {
-    // q and k_new arrive before the rotary embedding: rotate them in LDS, query column c (token
-    // c % T) and new token t at positions P + c % T and P + t; pairs (i, i + 32), i < 32
-    constexpr int kHalfRot = kRopeDims / 2;
-    const bool last = split == a.nsplit - 1;
-    const int n_q = ncols * kHalfRot, n_k = last ? a.T * kHalfRot : 0;
-    for (int u = tid; u < n_q + n_k; u += kDecNW * 64) {
-      const bool is_q = u < n_q;
-      const int uu = is_q ? u : u - n_q;
-      const int row = uu / kHalfRot, i = uu % kHalfRot;
-      const int pos = P + (is_q ? (cbase + row) % a.T : row);
-      char* base = is_q ? sq + row * Lds::kQStride * E::kBytes : smem + Lds::kQBytes + row * kDDQK * E::kBytes;
-      const f32x2 csn = *reinterpret_cast<const f32x2*>(a.rope + ((size_t)pos * kHalfRot + i) * 2);
-      if constexpr (E::kBytes == 2) {
-        uint16_t* e = reinterpret_cast<uint16_t*>(base);
-        const float x = __uint_as_float((uint32_t)e[i] << 16), y = __uint_as_float((uint32_t)e[i + kHalfRot] << 16);
-        e[i] = (uint16_t)bf16_bits(x * csn[0] - y * csn[1]);
-        e[i + kHalfRot] = (uint16_t)bf16_bits(y * csn[0] + x * csn[1]);
-      } else {
-        float* e = reinterpret_cast<float*>(base);
-        const float x = e[i], y = e[i + kHalfRot];
-        e[i] = x * csn[0] - y * csn[1];
-        e[i + kHalfRot] = y * csn[0] + x * csn[1];
-      }
-    }
+    rope_staged<E, NCB>(a, smem, tid, P, cbase, ncols, split == a.nsplit - 1);
     __syncthreads();
   }
 
@@ -548,6 +571,185 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
   }
 }
 
+// Sliding-window verify in one pass: at most 128 committed keys (window <= 129), at most 32 query
+// columns and at most 4 new tokens per (b, g), bf16 (the ring workload's shape). Wave w owns
+// committed-key block w (keys s0 + 32 w ..), so each column's maximum over all keys is known after
+// one exchange and no running max is needed:
+//   1. every wave forms S^T of its block and its column maxima; wave t also scores new token t
+//      on the VALU; maxima and new-token scores meet in LDS;
+//   2. every wave exponentiates its block against the common maximum and leaves P (bf16 MFMA
+//      fragments, over the no longer needed Q^T rows) and its column sums in LDS;
+//   3. wave w forms dv rows 32 w .. 32 w + 31 of O^T from all four blocks' V tiles and P, adds
+//      the new tokens and the sink, and writes them.
+// Against the general kernel this replaces the per-wave (m, l, acc) merge (64 KB of LDS traffic
+// and four barriers per workgroup) by two exchanges of 8 KB. A block past the committed keys
+// holds zero V rows and masked scores, so the products stay finite.
+template <bool ROPE>
+__global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_window_kernel(const DecodeArgs a) {
+  using E = BF16;
+  using Lds = DecodeLds<E, 1>;
+  __shared__ __attribute__((aligned(16))) char smem[Lds::kBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = blockIdx.y;  // one split, one column chunk
+  const int b = blockIdx.z;
+  const int ncols = a.ncols;
+
+  int P = a.cache_len[b];
+  P = P < 0 ? 0 : (P > a.max_len ? a.max_len : P);
+  const int off = a.cache_offset ? a.cache_offset[b] : 0;
+  const int s0 = max(0, P - a.window + 1);  // committed keys [s0, P), at most 128
+  const int s1 = P;
+  const int key0 = s0 + 32 * wave;
+  const bool has_keys = key0 < s1;
+
+  const size_t krow_bytes = (size_t)kDDQK * E::kBytes;
+  const size_t vrow_bytes = (size_t)kDDV * E::kBytes;
+  const size_t row0 = (size_t)b * a.C;
+
+  KeyRows<E> cur;
+  {
+    QStage<E, 1> st;
+    st.load(a, tid, b, g, 0, ncols);
+    if (has_keys) {
+      const int pos = min(key0 + col, s1 - 1);
+      int slot = (pos + off) % a.C;
+      slot += slot < 0 ? a.C : 0;
+      cur.load((const char*)a.k_cache + ((row0 + slot) * a.Hkv + g) * krow_bytes,
+               (const char*)a.v_cache + ((row0 + slot) * a.Hkv + g) * vrow_bytes, half);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KeyRows<E>::kKChunks; ++j) cur.k[j] = zero_chunk();
+#pragma unroll
+      for (int i = 0; i < KeyRows<E>::kVChunks; ++i) cur.v[i] = zero_chunk();
+    }
+    st.store(smem, tid, ncols, true, a.T);
+  }
+  char* sq = smem;
+  char* snew = smem + Lds::kQBytes;
+  char* work = snew + Lds::kNewBytes;
+  float* xm = reinterpret_cast<float*>(smem + (Lds::kBytes - kDecNW * 64 * 4 * 2));  // [wave][col]
+  float* xs = xm + kDecNW * 32;                                                      // [token][col]
+  float* xl = xs + kDecNW * 32;                                                      // [wave][col]
+  __syncthreads();  // Q^T and the new-token rows are in LDS
+  if constexpr (ROPE) {
+    rope_staged<E, 1>(a, smem, tid, P, 0, ncols, true);
+    __syncthreads();
+  }
+
+  const bool cvalid = col < ncols;
+  const int tq = cvalid ? col % a.T : 0;  // new token of this column
+  const float c = a.scale_log2;
+
+  // ---- 1. S^T of this wave's block, column maxima, new token `wave` ----
+  cur.store_v(work + wave * Lds::kVBytes, col, half);
+  f32x16 s = zero16();
+#pragma unroll
+  for (int kk = 0; kk < kDDQK / 16; ++kk) {
+    const bf16x8 qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                            sq + (col * Lds::kQStride + 16 * kk + 8 * half) * E::kBytes));
+    s = mma(cur.kfrag(kk), qf, s);
+  }
+  float bmax = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int pos = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+    s[r] = (pos < s1 && P + tq - pos < a.window) ? s[r] * c : -INFINITY;
+    bmax = fmaxf(bmax, s[r]);
+  }
+  bmax = halves_max(bmax);
+  if (half == 0) xm[wave * 32 + col] = bmax;
+  if (wave < a.T) {
+    const char* qrow = sq + col * Lds::kQStride * E::kBytes;
+    const char* krow = snew + wave * kDDQK * E::kBytes;
+    float dot = 0.f;
+    constexpr int kHalf = kDDQK / 2;
+#pragma unroll
+    for (int i = 0; i < kHalf / E::kPerChunk; ++i) {
+      const int e0 = kHalf * half + E::kPerChunk * i;
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + e0 * E::kBytes);
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + e0 * E::kBytes);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dot = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[j]), as_bf16x2(kv[j]), dot, false);
+    }
+    dot = halves_sum(dot);
+    const bool vis = cvalid && tq >= wave && tq - wave < a.window;
+    if (half == 0) xs[wave * 32 + col] = vis ? dot * c : -INFINITY;
+  }
+  __syncthreads();  // maxima and new-token scores are in LDS; Q^T is no longer read
+
+  // ---- 2. P of this block against the common maximum ----
+  const int head = cvalid ? a.hl.at(g * a.G + col / a.T) : 0;
+  const float sink_l2 = (a.sink && cvalid) ? a.sink[head] * kLog2e : -INFINITY;
+  float M = sink_l2;
+#pragma unroll
+  for (int w = 0; w < kDecNW; ++w) M = fmaxf(M, xm[w * 32 + col]);
+  float snt[kDecNW];
+#pragma unroll
+  for (int t = 0; t < kDecNW; ++t) {
+    snt[t] = t < a.T ? xs[t * 32 + col] : -INFINITY;
+    M = fmaxf(M, snt[t]);
+  }
+  const float M_use = (M == -INFINITY) ? 0.f : M;
+  float rs = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s[r] = fast_exp2(s[r] - M_use);
+    rs += s[r];
+  }
+  rs = halves_sum(rs);
+  char* sp = sq;  // P fragments [block][ks][lane], 16 bytes each, over the Q^T rows
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    st16(sp + ((wave * 2 + ks) * 64 + lane) * 16, __builtin_bit_cast(u32x4, frag_from_acc<E>(s, 8 * ks)));
+  if (half == 0) xl[wave * 32 + col] = rs;
+  __syncthreads();  // P fragments and block sums are in LDS
+
+  // ---- 3. dv rows 32 wave .. 32 wave + 31 of O^T over all blocks, new tokens, sink ----
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int kb = 0; kb < kDecNW; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, ld16(sp + ((kb * 2 + ks) * 64 + lane) * 16));
+      acc = mma(vt_frag_tr(work + kb * Lds::kVBytes, Lds::kVStride, wave, ks, lane), pf, acc);
+    }
+  float L = a.sink && cvalid ? fast_exp2(sink_l2 - M_use) : 0.f;
+#pragma unroll
+  for (int w = 0; w < kDecNW; ++w) L += xl[w * 32 + col];
+#pragma unroll
+  for (int t = 0; t < kDecNW; ++t) {
+    if (t >= a.T) break;
+    const float pn = fast_exp2(snt[t] - M_use);
+    L += pn;
+    const char* vrow = snew + Lds::kNewKBytes + t * kDDV * E::kBytes;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const u32x2 w2 = *reinterpret_cast<const u32x2*>(vrow + (32 * wave + 8 * gq + 4 * half) * 2);
+      acc[4 * gq + 0] = __builtin_fmaf(pn, __uint_as_float(w2[0] << 16), acc[4 * gq + 0]);
+      acc[4 * gq + 1] = __builtin_fmaf(pn, __uint_as_float(w2[0] & 0xFFFF0000u), acc[4 * gq + 1]);
+      acc[4 * gq + 2] = __builtin_fmaf(pn, __uint_as_float(w2[1] << 16), acc[4 * gq + 2]);
+      acc[4 * gq + 3] = __builtin_fmaf(pn, __uint_as_float(w2[1] & 0xFFFF0000u), acc[4 * gq + 3]);
+    }
+  }
+  if (!cvalid) return;
+  const float inv = 1.f / L;
+  char* orow = (char*)a.o + (((size_t)b * a.T + tq) * a.Hq + head) * kDDV * E::kBytes;
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+    u32x2 w2;
+    w2[0] = pack_bf16x2(acc[4 * gq] * inv, acc[4 * gq + 1] * inv);
+    w2[1] = pack_bf16x2(acc[4 * gq + 2] * inv, acc[4 * gq + 3] * inv);
+    *reinterpret_cast<u32x2*>(orow + (32 * wave + 8 * gq + 4 * half) * 2) = w2;
+  }
+  if (a.lse && wave == 0 && half == 0) a.lse[((size_t)b * a.T + tq) * a.Hq + head] = (M + fast_log2(L)) * kLn2;
+}
+
 // Folds the split partials and the sink (once) into O and LSE. A workgroup covers kCombCols query
 // columns of one (b, g); thread (column, quad) owns 4 consecutive dv of that column. Pass 1 takes
 // the max over the splits' m, pass 2 sums the rescaled l and acc, kCombUnroll splits at a time so
@@ -662,6 +864,12 @@ size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit) {
   return (size_t)B * Hkv * nsplit * ncols_pad * kRec * sizeof(float);
 }
 
+// The one-pass window kernel serves a single split of at most four 32-key blocks with at most 32
+// query columns and at most 4 new tokens.
+static bool window_kernel_fits(const DecodeArgs& a) {
+  return a.nsplit == 1 && a.keys_per_split <= 32 * kDecNW && a.ncols <= 32 && a.T <= kDecNW;
+}
+
 // With one column block (e.g. 8 query heads x 4 tokens) a wave holds few blocks and fewer
 // registers buy a second wave per SIMD; that beats prefetching (measured on the ring workload).
 #ifndef MIMO_DECODE_PREFETCH_1COL
@@ -672,6 +880,10 @@ template <bool ROPE>
 static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.nsplit, a.Hkv * a.n_chunks, a.B);
   const dim3 block(kDecNW * 64);
+  if (bf16 && window_kernel_fits(a)) {
+    hipLaunchKernelGGL((decode_window_kernel<ROPE>), grid, block, 0, stream, a);
+    return;
+  }
   const bool two = (a.n_chunks > 1 ? a.chunk_cols : a.ncols) > 32;
   if (bf16 && two)
     hipLaunchKernelGGL((decode_kernel<BF16, 2, true, ROPE>), grid, block, 0, stream, a);

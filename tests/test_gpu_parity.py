@@ -187,6 +187,37 @@ def test_decode_small_ring():
     check_decode(inp, 50)
 
 
+@pytest.mark.parametrize("T,Hq,Hkv", [(1, 64, 8), (2, 16, 1), (3, 64, 8), (4, 64, 8), (4, 12, 3)])
+def test_decode_window_129(T, Hq, Hkv):
+    # window 129: 128 committed keys, four full 32-key blocks in one pass; 12/3 heads x 4 tokens
+    # leaves 16 of the 32 query columns as padding
+    say(f"decode window 129 T={T} {Hq}/{Hkv}")
+    lens = np.array([0, 1, 31, 96, 97, 127, 128, 129, 130, 5000], np.int32)
+    inp = decode_inputs(35 + T, len(lens), T, Hq, Hkv, 192, 128, 140, 129, "bf16", len_range=(0, 1))
+    inp.cache_len = lens
+    check_decode(inp, int(lens.max()))
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_global_short_cache(T):
+    # a global layer whose linear cache holds at most 128 tokens runs the one-pass window kernel
+    say(f"decode global, cache <= 128, T={T}")
+    inp = decode_inputs(36 + T, 4, T, 64, 8, 192, 128, 128, 10**9, "bf16", ring_offsets=False,
+                        len_range=(0, 1))
+    inp.cache_len = np.array([0, 17, 100, 128], np.int32)
+    check_decode(inp, 128)
+
+
+def test_decode_ring_one_pass_equals_split():
+    say("decode ring: one pass vs two splits")
+    inp = decode_inputs(37, 6, 4, 64, 8, 192, 128, 128, 128, "bf16", len_range=(0, 3000))
+    one = run_decode(inp, 3000, num_splits=1)
+    two = run_decode(inp, 3000, num_splits=2)
+    for o in (one, two):
+        assert_output_close(o[0], o[2], "bf16")
+    assert np.abs(one[0] - two[0]).max() <= 2e-2
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("num_splits", [1, 2, 7, 0])
 def test_decode_global_splits(dtype, num_splits):
