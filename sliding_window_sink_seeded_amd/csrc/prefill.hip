@@ -25,6 +25,8 @@
 // prefill_kernel (generic: global attention, fp32, other shapes): streams the union of the
 //   workgroup's windows in BK-key blocks, double-buffered in LDS, with an online softmax whose
 //   running max is refreshed lazily (see below).
+#include <type_traits>
+
 #include "tiles.hpp"
 
 namespace mimo {
@@ -105,15 +107,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   wait_all();
   __syncthreads();
 
-  for (int ib = 0; ib < nblk; ++ib) {
+  // One block: stage the next block's loads, score, softmax, PV, store the next block, barrier.
+  // MASKED is a compile-time copy: blocks that every query of the tile sees in full run without
+  // any masking code (left to itself the compiler guards each score with its own branch).
+  auto block = [&](int ib, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int key0 = kstart + ib * BK;
     if (ib + 1 < nblk) st.load(kbase, vbase, krow_stride, vrow_stride, key0 + BK, a.L, tid, a.rope);
 
-    const bool skip = (key0 > p0 + kQT - 1) || (key0 + BK - 1 < p0 - a.window + 1) || (p0 >= a.L);
+    const bool skip = MASKED && ((key0 > p0 + kQT - 1) || (key0 + BK - 1 < p0 - a.window + 1) || (p0 >= a.L));
     if (!skip) {
       const char* sk = smem + (ib & 1) * Tile::kStageBytes;
       const char* sv = sk + Tile::kKBytes;
-      const bool need_mask = !((key0 + BK - 1 <= p0) && (p0 + kQT - 1 - key0 < a.window));
 
       f32x16 s[NSB];
 #pragma unroll
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
       for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if (need_mask) {
+          if constexpr (MASKED) {
             const int key = key0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
             const int d = qpos - key;
             s[sb][r] = (d >= 0 && d < a.window) ? s[sb][r] : -INFINITY;
@@ -174,6 +179,29 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
 
     if (ib + 1 < nblk) st.store(smem + ((ib + 1) & 1) * Tile::kStageBytes, tid);
     __syncthreads();
+  };
+
+  // Blocks [ib_a, ib_b) are seen in full by every query of this wave's tile: all their keys are
+  // at or before the tile's first position and within the window of its last one. Waves may
+  // differ in the range: every wave still runs all nblk blocks with the same stage loads, stores
+  // and barriers, only its own math takes one copy or the other. Tiles past L take the masked
+  // copy (which skips them).
+  int ib_a = nblk, ib_b = nblk;
+  if (p0 < a.L) {
+    const int hi_num = p0 - (BK - 1) - kstart;  // ib < hi  <=>  key0 + BK - 1 <= p0
+    const int hi = hi_num >= 0 ? hi_num / BK + 1 : 0;
+    const long long lo_num = (long long)p0 + kQT - a.window - kstart;  // ib >= lo  <=>  p0 + kQT - 1 - key0 < window
+    const int lo = lo_num <= 0 ? 0 : (int)min<long long>((lo_num + BK - 1) / BK, nblk);
+    ib_a = min(lo, nblk);
+    ib_b = min(max(hi, ib_a), nblk);
+  }
+  ib_a = __builtin_amdgcn_readfirstlane(ib_a);
+  ib_b = __builtin_amdgcn_readfirstlane(ib_b);
+  // runs: masked [0, ib_a), mask-free [ib_a, ib_b), masked [ib_b, nblk); one call site per copy
+  for (int ib = 0; ib < nblk;) {
+    const int stop = ib < ib_a ? ib_a : (ib < ib_b ? ib : nblk);
+    for (; ib < stop; ++ib) block(ib, std::true_type{});
+    for (; ib < ib_b; ++ib) block(ib, std::false_type{});
   }
 
   const bool valid = qpos < a.L;
