@@ -100,11 +100,21 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   const int kstart = (K0 / BK) * BK;
   const int nblk = (P1 - kstart + BK - 1) / BK;
 
+  // bf16 64-key blocks go global -> LDS directly (no staging registers); the others through
+  // registers
+  constexpr bool kDMA = E::kBytes == 2 && BK == 64 && !ROPE;
   KVStager<E, NT, BK, ROPE ? kRopeMem : kRopeNone> st;
-  st.init(krow_stride, vrow_stride, tid);
-  st.load(kbase, vbase, krow_stride, vrow_stride, kstart, a.L, tid, a.rope);
-  st.store(smem, tid);
-  wait_all();
+  KVStagerDMA<NW, 64> dma;  // used only when kDMA (BK == 64)
+  if constexpr (kDMA) {
+    dma.init(krow_stride, vrow_stride, wave, lane);
+    dma.load(smem, kbase, vbase, krow_stride, vrow_stride, kstart, a.L, wave, lane);
+    wait_vm();
+  } else {
+    st.init(krow_stride, vrow_stride, tid);
+    st.load(kbase, vbase, krow_stride, vrow_stride, kstart, a.L, tid, a.rope);
+    st.store(smem, tid);
+    wait_all();
+  }
   __syncthreads();
 
   // One block: stage the next block's loads, score, softmax, PV, store the next block, barrier.
@@ -113,7 +123,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   auto block = [&](int ib, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int key0 = kstart + ib * BK;
-    if (ib + 1 < nblk) st.load(kbase, vbase, krow_stride, vrow_stride, key0 + BK, a.L, tid, a.rope);
+    if (ib + 1 < nblk) {
+      if constexpr (kDMA)
+        dma.load(smem + ((ib + 1) & 1) * Tile::kStageBytes, kbase, vbase, krow_stride, vrow_stride, key0 + BK,
+                 a.L, wave, lane);
+      else
+        st.load(kbase, vbase, krow_stride, vrow_stride, key0 + BK, a.L, tid, a.rope);
+    }
 
     const bool skip = MASKED && ((key0 > p0 + kQT - 1) || (key0 + BK - 1 < p0 - a.window + 1) || (p0 >= a.L));
     if (!skip) {
@@ -177,7 +193,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
       }
     }
 
-    if (ib + 1 < nblk) st.store(smem + ((ib + 1) & 1) * Tile::kStageBytes, tid);
+    if constexpr (kDMA) {
+      wait_vm();  // this wave's loads of the next stage have landed
+    } else {
+      if (ib + 1 < nblk) st.store(smem + ((ib + 1) & 1) * Tile::kStageBytes, tid);
+    }
     __syncthreads();
   };
 
