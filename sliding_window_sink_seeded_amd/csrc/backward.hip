@@ -21,6 +21,8 @@
 //   every wave: S = Q K^T, P, dP = dO V^T, dS; dV^T += dO^T P and dK^T += Q^T dS take P and dS
 //   straight from the accumulators.
 // bwd_sink_kernel: sums the per-tile sink partials of each head in a fixed order.
+#include <type_traits>
+
 #include "tiles.hpp"
 
 namespace mimo {
@@ -133,15 +135,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
   wait_all();
   __syncthreads();
 
-  for (int ib = 0; ib < nblk; ++ib) {
+  // One block; MASKED is a compile-time copy, the mask-free one serves blocks that every query of
+  // this wave's tile sees in full (see the prefill kernel: waves may differ in the range, all run
+  // every block with the same stage loads, stores and barriers).
+  auto block = [&](int ib, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int key0 = kstart + ib * BK;
     if (ib + 1 < nblk) st.load(kbase, vbase, krow_stride, vrow_stride, key0 + BK, a.L, tid);
 
-    const bool skip = (key0 > p0 + kQT - 1) || (key0 + BK - 1 < p0 - a.window + 1) || (p0 >= a.L);
+    const bool skip = MASKED && ((key0 > p0 + kQT - 1) || (key0 + BK - 1 < p0 - a.window + 1) || (p0 >= a.L));
     if (!skip) {
       const char* sk = smem + (ib & 1) * Tile::kStageBytes;
       const char* sv = sk + Tile::kKBytes;
-      const bool need_mask = !((key0 + BK - 1 <= p0) && (p0 + kQT - 1 - key0 < a.window));
 
       f32x16 s[NSB], dp[NSB];
 #pragma unroll
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = fast_exp2(__builtin_fmaf(s[sb][r], c, -lse2));
-          if (need_mask) {
+          if constexpr (MASKED) {
             const int key = key0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
             const int d = qpos - key;
             p = (d >= 0 && d < a.window) ? p : 0.f;
@@ -182,6 +187,25 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
 
     if (ib + 1 < nblk) st.store(smem + ((ib + 1) & 1) * Tile::kStageBytes, tid);
     __syncthreads();
+  };
+
+  // blocks [ib_a, ib_b): every key at or before the tile's first row and within the window of
+  // its last one
+  int ib_a = nblk, ib_b = nblk;
+  if (p0 < a.L) {
+    const int hi_num = p0 - (BK - 1) - kstart;
+    const int hi = hi_num >= 0 ? hi_num / BK + 1 : 0;
+    const long long lo_num = (long long)p0 + kQT - a.window - kstart;
+    const int lo = lo_num <= 0 ? 0 : (int)min<long long>((lo_num + BK - 1) / BK, nblk);
+    ib_a = min(lo, nblk);
+    ib_b = min(max(hi, ib_a), nblk);
+  }
+  ib_a = __builtin_amdgcn_readfirstlane(ib_a);
+  ib_b = __builtin_amdgcn_readfirstlane(ib_b);
+  for (int ib = 0; ib < nblk;) {
+    const int stop = ib < ib_a ? ib_a : (ib < ib_b ? ib : nblk);
+    for (; ib < stop; ++ib) block(ib, std::true_type{});
+    for (; ib < ib_b; ++ib) block(ib, std::false_type{});
   }
 
   char* dqrow = (char*)a.dq + row * kDQK * E::kBytes;
