@@ -128,11 +128,20 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
   const int kstart = (K0 / BK) * BK;
   const int nblk = (P1 - kstart + BK - 1) / BK;
 
+  // bf16 blocks go global -> LDS directly (no staging registers), fp32 through registers
+  constexpr bool kDMA = E::kBytes == 2;
   KVStager<E, NT, BK, kRopeNone, kVRows> st;
-  st.init(krow_stride, vrow_stride, tid);
-  st.load(kbase, vbase, krow_stride, vrow_stride, kstart, a.L, tid);
-  st.store(smem, tid);
-  wait_all();
+  KVStagerDMA<NW, BK, kVRows> dma;
+  if constexpr (kDMA) {
+    dma.init(krow_stride, vrow_stride, wave, lane);
+    dma.load(smem, kbase, vbase, krow_stride, vrow_stride, kstart, a.L, wave, lane);
+    wait_vm();
+  } else {
+    st.init(krow_stride, vrow_stride, tid);
+    st.load(kbase, vbase, krow_stride, vrow_stride, kstart, a.L, tid);
+    st.store(smem, tid);
+    wait_all();
+  }
   __syncthreads();
 
   // One block; MASKED is a compile-time copy, the mask-free one serves blocks that every query of
@@ -141,7 +150,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
   auto block = [&](int ib, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int key0 = kstart + ib * BK;
-    if (ib + 1 < nblk) st.load(kbase, vbase, krow_stride, vrow_stride, key0 + BK, a.L, tid);
+    if (ib + 1 < nblk) {
+      if constexpr (kDMA)
+        dma.load(smem + ((ib + 1) & 1) * Tile::kStageBytes, kbase, vbase, krow_stride, vrow_stride, key0 + BK,
+                 a.L, wave, lane);
+      else
+        st.load(kbase, vbase, krow_stride, vrow_stride, key0 + BK, a.L, tid);
+    }
 
     const bool skip = MASKED && ((key0 > p0 + kQT - 1) || (key0 + BK - 1 < p0 - a.window + 1) || (p0 >= a.L));
     if (!skip) {
@@ -185,7 +200,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
       }
     }
 
-    if (ib + 1 < nblk) st.store(smem + ((ib + 1) & 1) * Tile::kStageBytes, tid);
+    if constexpr (kDMA) {
+      wait_vm();  // this wave's loads of the next stage have landed
+    } else {
+      if (ib + 1 < nblk) st.store(smem + ((ib + 1) & 1) * Tile::kStageBytes, tid);
+    }
     __syncthreads();
   };
 

@@ -178,29 +178,34 @@ struct KVStager {
 
 // Global -> LDS staging of one bf16 K/V block without a register pass (the 16-byte
 // global_load_lds of gfx950: lane i of one instruction writes LDS bytes [16 i, 16 i + 16) past the
-// instruction's base). The stage keeps PrefillTile's padded rows: instruction u covers LDS chunks
-// 64 u .. 64 u + 63 of the K region (25 chunks per row: 24 of data, 1 of padding) or of the V
-// region (18 per row: 16 + 2); a lane whose chunk is padding re-reads a data chunk of its row, so
-// every lane's address is valid. With BK = 64 both regions are whole instructions (25 and 18),
-// dealt round-robin to the NW waves. Rows at or past L are read from row L - 1. The caller waits
-// for the loads (vmcnt) before the barrier that publishes the stage.
-template <int NW, int BK>
+// instruction's base; lanes that are switched off write nothing). The stage keeps PrefillTile's
+// padded rows: instruction u covers LDS chunks 64 u .. 64 u + 63 of the K region (kKRow chunks per
+// row, the last one padding) or of the V region; a lane whose chunk is padding re-reads a data
+// chunk of its row, so every lane's address is valid, and in a region's last instruction the
+// lanes past the region are switched off. The instructions are dealt round-robin to the NW waves.
+// Rows at or past L are read from row L - 1. The caller waits for the loads (vmcnt) before the
+// barrier that publishes the stage.
+template <int NW, int BK, int VL = kVRowsTr>
 struct KVStagerDMA {
-  using Tile = PrefillTile<BF16, BK, kVRowsTr>;
+  using Tile = PrefillTile<BF16, BK, VL>;
   static constexpr int kKRow = Tile::kKStride * 2 / 16, kVRow = Tile::kVStride * 2 / 16;  // chunks per row
-  static constexpr int kKInst = BK * kKRow / 64, kVInst = BK * kVRow / 64;
-  static_assert(BK * kKRow % 64 == 0 && BK * kVRow % 64 == 0, "whole instructions per region");
-  static_assert(kKInst * 1024 == Tile::kKBytes && kVInst * 1024 == Tile::kVBytes, "regions tile the stage");
+  static constexpr int kKChunks = BK * kKRow, kVChunks = BK * kVRow;
+  static constexpr int kKInst = (kKChunks + 63) / 64, kVInst = (kVChunks + 63) / 64;
+  static_assert(kKChunks * 16 == Tile::kKBytes && kVChunks * 16 == Tile::kVBytes, "regions tile the stage");
+  static_assert(Tile::kVRowMajor, "row-major V");
   static constexpr int kInst = kKInst + kVInst;
   static constexpr int kPer = (kInst + NW - 1) / NW;  // instruction slots per wave
   uint32_t off[kPer];  // byte offset of this lane's chunk from the block's first row (row 0 = key0)
 
-  __device__ static void row_chunk(int u, int lane, int& row, int& ch, bool& is_k) {
-    is_k = u < kKInst;
+  // row and data chunk of lane `lane` in instruction u; false for a lane past its region
+  __device__ static bool row_chunk(int u, int lane, int& row, int& ch) {
+    const bool is_k = u < kKInst;
     const int p = 64 * (is_k ? u : u - kKInst) + lane;
-    const int per = is_k ? kKRow : kVRow;
-    row = p / per;
-    ch = min(p % per, (is_k ? kDQK : kDV) / 8 - 1);
+    const int n = is_k ? kKChunks : kVChunks, per = is_k ? kKRow : kVRow;
+    const int pc = min(p, n - 1);
+    row = pc / per;
+    ch = min(pc % per, (is_k ? kDQK : kDV) / 8 - 1);
+    return p < n;
   }
 
   __device__ __forceinline__ void init(size_t kstride, size_t vstride, int wave, int lane) {
@@ -208,9 +213,8 @@ struct KVStagerDMA {
     for (int i = 0; i < kPer; ++i) {
       const int u = min(wave + i * NW, kInst - 1);
       int row, ch;
-      bool is_k;
-      row_chunk(u, lane, row, ch, is_k);
-      off[i] = (uint32_t)(row * (is_k ? kstride : vstride) + ch * 16);
+      row_chunk(u, lane, row, ch);
+      off[i] = (uint32_t)(row * (u < kKInst ? kstride : vstride) + ch * 16);
     }
   }
 
@@ -224,15 +228,14 @@ struct KVStagerDMA {
       if (u >= kInst) break;  // uniform per wave
       const bool is_k = u < kKInst;
       const char* p = (is_k ? kbase + (size_t)key0 * kstride : vbase + (size_t)key0 * vstride) + off[i];
-      if (tail) {
-        int row, ch;
-        bool k2;
-        row_chunk(u, lane, row, ch, k2);
-        p += ((size_t)min(key0 + row, L - 1) - (key0 + row)) * (is_k ? kstride : vstride);
-      }
+      int row, ch;
+      const bool active = row_chunk(u, lane, row, ch);
+      if (tail) p += ((size_t)min(key0 + row, L - 1) - (key0 + row)) * (is_k ? kstride : vstride);
       char* dst = stage + (is_k ? 1024 * u : Tile::kKBytes + 1024 * (u - kKInst));
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)p,
-                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      const bool partial = is_k ? (u == kKInst - 1 && kKChunks % 64) : (u == kInst - 1 && kVChunks % 64);
+      if (!partial || active)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)p,
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   }
 };
