@@ -572,19 +572,22 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
 }
 
 // Sliding-window verify in one pass: at most 128 committed keys (window <= 129), at most 32 query
-// columns and at most 4 new tokens per (b, g), bf16 (the ring workload's shape). Wave w owns
+// columns per workgroup (a column chunk of the G*T columns of (b, g)) and at most 4 new tokens, or
+// 8 with EXT (block drafts), bf16 (the ring workloads' shape). Wave w owns
 // committed-key block w (keys s0 + 32 w ..), so each column's maximum over all keys is known after
 // one exchange and no running max is needed:
-//   1. every wave forms S^T of its block and its column maxima; wave t also scores new token t
-//      on the VALU; maxima and new-token scores meet in LDS;
+//   1. every wave forms S^T of its block and its column maxima; wave w also scores new tokens w
+//      and w + 4 on the VALU; maxima and new-token scores meet in LDS;
 //   2. every wave exponentiates its block against the common maximum and leaves P (bf16 MFMA
 //      fragments, over the no longer needed Q^T rows) and its column sums in LDS;
 //   3. wave w forms dv rows 32 w .. 32 w + 31 of O^T from all four blocks' V tiles and P, adds
 //      the new tokens and the sink, and writes them.
 // Against the general kernel this replaces the per-wave (m, l, acc) merge (64 KB of LDS traffic
 // and four barriers per workgroup) by two exchanges of 8 KB. A block past the committed keys
-// holds zero V rows and masked scores, so the products stay finite.
-template <bool ROPE>
+// holds zero V rows and masked scores, so the products stay finite. Tokens 4..7 (EXT): LDS is full
+// during step 1, so their K rows are fetched into registers at kernel start and their V rows are
+// written after the first barrier next to the P fragments.
+template <bool ROPE, bool EXT>
 __global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_window_kernel(const DecodeArgs a) {
   using E = BF16;
@@ -596,9 +599,11 @@ void decode_window_kernel(const DecodeArgs a) {
   const int half = lane >> 5;
   const int col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = blockIdx.y;  // one split, one column chunk
+  const int chunk = blockIdx.y % a.n_chunks;  // one split
+  const int g = blockIdx.y / a.n_chunks;
   const int b = blockIdx.z;
-  const int ncols = a.ncols;
+  const int cbase = chunk * a.chunk_cols;  // this workgroup's columns: cbase + [0, ncols)
+  const int ncols = min(a.chunk_cols, a.ncols - cbase);
 
   int P = a.cache_len[b];
   P = P < 0 ? 0 : (P > a.max_len ? a.max_len : P);
@@ -612,10 +617,28 @@ void decode_window_kernel(const DecodeArgs a) {
   const size_t vrow_bytes = (size_t)kDDV * E::kBytes;
   const size_t row0 = (size_t)b * a.C;
 
+  // EXT: K row of new token wave + 4 (this lane half's 96 elements) and one 16-byte chunk of the
+  // V rows of tokens 4..7 per thread, fetched now, used in steps 1 and 2
+  constexpr int kHalfChunks = kDDQK / 2 / E::kPerChunk;
+  u32x4 kx[EXT ? kHalfChunks : 1];
+  u32x4 vx = zero_chunk();
+  const int tok_hi = wave + 4;
+  const int nvx = EXT ? (a.T > 4 ? (a.T - 4) * (kDDV / E::kPerChunk) : 0) : 0;  // V chunks of tokens 4..T-1
+  if constexpr (EXT) {
+    const int t = min(tok_hi, a.T - 1);
+    const char* krow = (const char*)a.k_new + (((size_t)b * a.T + t) * a.Hkv + g) * krow_bytes + half * (kDDQK / 2) * E::kBytes;
+#pragma unroll
+    for (int i = 0; i < kHalfChunks; ++i) kx[i] = ld16(krow + 16 * i);
+    if (tid < nvx) {
+      const int tv = 4 + tid / (kDDV / E::kPerChunk), ch = tid % (kDDV / E::kPerChunk);
+      vx = ld16((const char*)a.v_new + (((size_t)b * a.T + tv) * a.Hkv + g) * vrow_bytes + ch * 16);
+    }
+  }
+
   KeyRows<E> cur;
   {
     QStage<E, 1> st;
-    st.load(a, tid, b, g, 0, ncols);
+    st.load(a, tid, b, g, cbase, ncols);
     if (has_keys) {
       const int pos = min(key0 + col, s1 - 1);
       int slot = (pos + off) % a.C;
@@ -634,16 +657,18 @@ void decode_window_kernel(const DecodeArgs a) {
   char* snew = smem + Lds::kQBytes;
   char* work = snew + Lds::kNewBytes;
   float* xm = reinterpret_cast<float*>(smem + (Lds::kBytes - kDecNW * 64 * 4 * 2));  // [wave][col]
-  float* xs = xm + kDecNW * 32;                                                      // [token][col]
-  float* xl = xs + kDecNW * 32;                                                      // [wave][col]
+  float* xs = xm + kDecNW * 32;                                                      // [token][col], 8 tokens
+  float* xl = xs + 2 * kDecNW * 32;                                                  // [wave][col]
+  static_assert(4 * kDecNW * 32 * 4 <= kDecNW * 64 * 4 * 2, "exchange area");
   __syncthreads();  // Q^T and the new-token rows are in LDS
   if constexpr (ROPE) {
-    rope_staged<E, 1>(a, smem, tid, P, 0, ncols, true);
+    rope_staged<E, 1>(a, smem, tid, P, cbase, ncols, true);
     __syncthreads();
   }
 
   const bool cvalid = col < ncols;
-  const int tq = cvalid ? col % a.T : 0;  // new token of this column
+  const int cg = cbase + col;              // column within the G*T columns of (b, g)
+  const int tq = cvalid ? cg % a.T : 0;   // new token of this column
   const float c = a.scale_log2;
 
   // ---- 1. S^T of this wave's block, column maxima, new token `wave` ----
@@ -664,34 +689,37 @@ void decode_window_kernel(const DecodeArgs a) {
   }
   bmax = halves_max(bmax);
   if (half == 0) xm[wave * 32 + col] = bmax;
-  if (wave < a.T) {
+  // score of new token t for this lane's column: q . k over this half's 96 elements (K chunks from
+  // `krow` in LDS, or from registers for tokens 4..7), then across halves
+  auto new_score = [&](int t, const char* krow, bool in_regs) {
     const char* qrow = sq + col * Lds::kQStride * E::kBytes;
-    const char* krow = snew + wave * kDDQK * E::kBytes;
     float dot = 0.f;
-    constexpr int kHalf = kDDQK / 2;
 #pragma unroll
-    for (int i = 0; i < kHalf / E::kPerChunk; ++i) {
-      const int e0 = kHalf * half + E::kPerChunk * i;
+    for (int i = 0; i < kHalfChunks; ++i) {
+      const int e0 = (kDDQK / 2) * half + E::kPerChunk * i;
       const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + e0 * E::kBytes);
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + e0 * E::kBytes);
+      const u32x4 kv = in_regs ? kx[EXT ? i : 0] : *reinterpret_cast<const u32x4*>(krow + e0 * E::kBytes);
 #pragma unroll
       for (int j = 0; j < 4; ++j) dot = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[j]), as_bf16x2(kv[j]), dot, false);
     }
     dot = halves_sum(dot);
-    const bool vis = cvalid && tq >= wave && tq - wave < a.window;
-    if (half == 0) xs[wave * 32 + col] = vis ? dot * c : -INFINITY;
-  }
+    const bool vis = cvalid && tq >= t && tq - t < a.window;
+    if (half == 0) xs[t * 32 + col] = vis ? dot * c : -INFINITY;
+  };
+  if (wave < a.T) new_score(wave, snew + wave * kDDQK * E::kBytes, false);
+  if (EXT && tok_hi < a.T) new_score(tok_hi, nullptr, true);
   __syncthreads();  // maxima and new-token scores are in LDS; Q^T is no longer read
 
   // ---- 2. P of this block against the common maximum ----
-  const int head = cvalid ? a.hl.at(g * a.G + col / a.T) : 0;
+  const int head = cvalid ? a.hl.at(g * a.G + cg / a.T) : 0;
   const float sink_l2 = (a.sink && cvalid) ? a.sink[head] * kLog2e : -INFINITY;
   float M = sink_l2;
 #pragma unroll
   for (int w = 0; w < kDecNW; ++w) M = fmaxf(M, xm[w * 32 + col]);
-  float snt[kDecNW];
+  constexpr int kNT = EXT ? 2 * kDecNW : kDecNW;  // new tokens this instance handles
+  float snt[kNT];
 #pragma unroll
-  for (int t = 0; t < kDecNW; ++t) {
+  for (int t = 0; t < kNT; ++t) {
     snt[t] = t < a.T ? xs[t * 32 + col] : -INFINITY;
     M = fmaxf(M, snt[t]);
   }
@@ -708,7 +736,11 @@ void decode_window_kernel(const DecodeArgs a) {
   for (int ks = 0; ks < 2; ++ks)
     st16(sp + ((wave * 2 + ks) * 64 + lane) * 16, __builtin_bit_cast(u32x4, frag_from_acc<E>(s, 8 * ks)));
   if (half == 0) xl[wave * 32 + col] = rs;
-  __syncthreads();  // P fragments and block sums are in LDS
+  // V rows of tokens 4..7 next to the P fragments, in the part of the Q^T rows P leaves free
+  char* snew_hi = sq + kDecNW * 2 * 64 * 16;
+  static_assert(kDecNW * 2 * 64 * 16 + 4 * kDDV * 2 <= Lds::kQBytes, "tokens 4..7 fit beside P");
+  if (EXT && tid < nvx) st16(snew_hi + tid * 16, vx);
+  __syncthreads();  // P fragments, block sums and the V rows of tokens 4..7 are in LDS
 
   // ---- 3. dv rows 32 wave .. 32 wave + 31 of O^T over all blocks, new tokens, sink ----
   f32x16 acc = zero16();
@@ -723,11 +755,11 @@ void decode_window_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int w = 0; w < kDecNW; ++w) L += xl[w * 32 + col];
 #pragma unroll
-  for (int t = 0; t < kDecNW; ++t) {
+  for (int t = 0; t < kNT; ++t) {
     if (t >= a.T) break;
     const float pn = fast_exp2(snt[t] - M_use);
     L += pn;
-    const char* vrow = snew + Lds::kNewKBytes + t * kDDV * E::kBytes;
+    const char* vrow = t < 4 ? snew + Lds::kNewKBytes + t * kDDV * E::kBytes : snew_hi + (t - 4) * kDDV * E::kBytes;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       const u32x2 w2 = *reinterpret_cast<const u32x2*>(vrow + (32 * wave + 8 * gq + 4 * half) * 2);
@@ -865,9 +897,10 @@ size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit) {
 }
 
 // The one-pass window kernel serves a single split of at most four 32-key blocks with at most 32
-// query columns and at most 4 new tokens.
+// query columns per workgroup and at most 4 new tokens (8 without RoPE).
 static bool window_kernel_fits(const DecodeArgs& a) {
-  return a.nsplit == 1 && a.keys_per_split <= 32 * kDecNW && a.ncols <= 32 && a.T <= kDecNW;
+  const bool cols = a.ncols <= 32 || a.chunk_cols == 32;  // every workgroup's chunk fits one column block
+  return a.nsplit == 1 && a.keys_per_split <= 32 * kDecNW && cols && (a.T <= kDecNW || (a.T <= 2 * kDecNW && !a.rope));
 }
 
 // With one column block (e.g. 8 query heads x 4 tokens) a wave holds few blocks and fewer
@@ -881,7 +914,10 @@ static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t str
   const dim3 grid(a.nsplit, a.Hkv * a.n_chunks, a.B);
   const dim3 block(kDecNW * 64);
   if (bf16 && window_kernel_fits(a)) {
-    hipLaunchKernelGGL((decode_window_kernel<ROPE>), grid, block, 0, stream, a);
+    if (a.T > kDecNW)
+      hipLaunchKernelGGL((decode_window_kernel<false, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_window_kernel<ROPE, false>), grid, block, 0, stream, a);
     return;
   }
   const bool two = (a.n_chunks > 1 ? a.chunk_cols : a.ncols) > 32;
