@@ -599,9 +599,20 @@ void decode_window_kernel(const DecodeArgs a) {
   const int half = lane >> 5;
   const int col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int chunk = blockIdx.y % a.n_chunks;  // one split
-  const int g = blockIdx.y / a.n_chunks;
-  const int b = blockIdx.z;
+  // one split. Column chunks of one (b, g) read the same K/V rows: workgroups are dealt to the
+  // XCDs round-robin by linear index, so with several chunks the index is remapped to put the
+  // chunks of one (b, g) eight apart (same XCD, same L2, launched together) when the (b, g) pairs
+  // come in whole groups of eight.
+  int chunk = blockIdx.y % a.n_chunks, g = blockIdx.y / a.n_chunks, b = blockIdx.z;
+  const int pairs = a.B * a.Hkv;
+  if (a.n_chunks > 1 && pairs % 8 == 0) {
+    const int id = blockIdx.y + gridDim.y * blockIdx.z;
+    const int q = id / 8;
+    chunk = q % a.n_chunks;
+    const int pair = (q / a.n_chunks) * 8 + id % 8;
+    g = pair % a.Hkv;
+    b = pair / a.Hkv;
+  }
   const int cbase = chunk * a.chunk_cols;  // this workgroup's columns: cbase + [0, ncols)
   const int ncols = min(a.chunk_cols, a.ncols - cbase);
 
