@@ -9,11 +9,11 @@
 #include "../../include/mimo_attn.h"
 #include "launch.hpp"
 
-#ifndef MIMO_DECODE_CHUNK_1SPLIT
-#define MIMO_DECODE_CHUNK_1SPLIT 32
-#endif
-
 namespace {
+
+// Query columns per workgroup of a single-pass decode with more than 32 columns (see decode_impl).
+constexpr int kChunkCols1Split = 32;
+
 
 thread_local std::string g_err;
 
@@ -343,7 +343,7 @@ int decode_impl(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
   // columns takes chunks of 32: the one-block kernel keeps two waves per SIMD, which beats
   // reading the short K/V history once with the 64-column kernel (8 heads x 8 tokens: 107 vs
   // 147 us).
-  a.chunk_cols = (plan.nsplit == 1 && a.ncols > 32) ? MIMO_DECODE_CHUNK_1SPLIT : mimo::kMaxCols;
+  a.chunk_cols = (plan.nsplit == 1 && a.ncols > 32) ? kChunkCols1Split : mimo::kMaxCols;
   a.n_chunks = (a.ncols + a.chunk_cols - 1) / a.chunk_cols;
   if ((long long)a.Hkv * a.n_chunks > 65535) return fail(MIMO_EUNSUPPORTED, "too many KV heads x column chunks");
   if (int rc = group_heads(Hq, Hkv, kv_head_of_q, &a.hl)) return rc;

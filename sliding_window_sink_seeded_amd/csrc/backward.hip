@@ -233,9 +233,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
 
 // ---------------------------------------------------------------------------------- dK/dV kernel
 
-#ifndef MIMO_DKDV_SGB
-#define MIMO_DKDV_SGB 6
-#endif
+// LDS operand reads of the dK/dV step are issued this many MFMAs ahead of their products (one
+// wave per SIMD cannot hide an LDS round trip behind another wave's work).
+constexpr int kDkdvReadAhead = 6;
 
 // LDS stage of one step: Q rows [32][kQS], dO rows [32][kOS], then lse * log2(e) [32] and D [32].
 // Row strides are padded so that both the 16-byte row reads and the transposing reads of the MFMA
@@ -439,25 +439,22 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
         acck[t] = mma(f, dsf, (first && ks == 0) ? zero16() : acck[t]);
       }
     }
-#if MIMO_DKDV_SGB
-    // Issue order: LDS operand reads run several MFMAs ahead (one wave per SIMD cannot hide an
-    // LDS round trip behind another wave). Phase 1: 20 row reads for 20 MFMAs; phase 2: 40
-    // transposing reads (two per fragment) for 20 MFMAs.
-    __builtin_amdgcn_sched_group_barrier(0x100, MIMO_DKDV_SGB, 0);
+    // Issue order: LDS operand reads run kDkdvReadAhead MFMAs ahead. Phase 1: 20 row reads for 20
+    // MFMAs; phase 2: 40 transposing reads (two per fragment) for 20 MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, kDkdvReadAhead, 0);
 #pragma unroll
-    for (int i = 0; i < 20 - MIMO_DKDV_SGB; ++i) {
+    for (int i = 0; i < 20 - kDkdvReadAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, MIMO_DKDV_SGB, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MIMO_DKDV_SGB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kDkdvReadAhead, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDkdvReadAhead, 0);
 #pragma unroll
-    for (int i = 0; i < 20 - MIMO_DKDV_SGB; ++i) {
+    for (int i = 0; i < 20 - kDkdvReadAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, MIMO_DKDV_SGB, 0);
-#endif
+    __builtin_amdgcn_sched_group_barrier(0x008, kDkdvReadAhead, 0);
   };
 
   // Step 0 is peeled so that the accumulators start as MFMA results. The scheduling barriers

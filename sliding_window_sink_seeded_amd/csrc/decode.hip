@@ -915,10 +915,9 @@ static bool window_kernel_fits(const DecodeArgs& a) {
 }
 
 // With one column block (e.g. 8 query heads x 4 tokens) a wave holds few blocks and fewer
-// registers buy a second wave per SIMD; that beats prefetching (measured on the ring workload).
-#ifndef MIMO_DECODE_PREFETCH_1COL
-#define MIMO_DECODE_PREFETCH_1COL false
-#endif
+// registers buy a second wave per SIMD; that beats prefetching (measured on the ring workload),
+// so the one-column kernel does not prefetch.
+constexpr bool kPrefetch1Col = false;
 
 template <bool ROPE>
 static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t stream) {
@@ -935,7 +934,7 @@ static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t str
   if (bf16 && two)
     hipLaunchKernelGGL((decode_kernel<BF16, 2, true, ROPE>), grid, block, 0, stream, a);
   else if (bf16)
-    hipLaunchKernelGGL((decode_kernel<BF16, 1, MIMO_DECODE_PREFETCH_1COL, ROPE>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<BF16, 1, kPrefetch1Col, ROPE>), grid, block, 0, stream, a);
   else if (two)
     hipLaunchKernelGGL((decode_kernel<F32, 2, false, ROPE>), grid, block, 0, stream, a);
   else

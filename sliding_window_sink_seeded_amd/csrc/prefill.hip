@@ -477,23 +477,21 @@ static hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-#ifndef MIMO_SWA_WG_PER_CU
-#define MIMO_SWA_WG_PER_CU 4
-#endif
-#ifndef MIMO_SWA_MIN_TILES
-#define MIMO_SWA_MIN_TILES 8
-#endif
+// Segment sizing of the ring kernel: about this many workgroups per compute unit over the grid,
+// and never fewer than this many tiles per segment (each segment re-reads a window of halo).
+constexpr int kSwaWgPerCu = 4;
+constexpr int kSwaMinTiles = 8;
 
 template <int NB>
 static hipError_t launch_swa(PrefillArgs a, hipStream_t stream) {
   const int n_tiles = (a.L + kQT - 1) / kQT;
   const long long units = (long long)a.B * a.Hkv * a.n_hchunks;
   // spread the tiles of every (b, g, head chunk) over segments so that about
-  // MIMO_SWA_WG_PER_CU workgroups per compute unit run in total
-  long long segs = (MIMO_SWA_WG_PER_CU * 256LL + units - 1) / units;
+  // kSwaWgPerCu workgroups per compute unit run in total
+  long long segs = (kSwaWgPerCu * 256LL + units - 1) / units;
   segs = segs < 1 ? 1 : segs;
   long long per = (n_tiles + segs - 1) / segs;
-  if (per < MIMO_SWA_MIN_TILES) per = MIMO_SWA_MIN_TILES;
+  if (per < kSwaMinTiles) per = kSwaMinTiles;
   a.tiles_per_wg = (int)per;
   a.n_segments = (int)((n_tiles + per - 1) / per);
   const long long n_wg = units * a.n_segments;
