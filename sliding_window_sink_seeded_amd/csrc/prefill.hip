@@ -477,9 +477,11 @@ static hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Segment sizing of the ring kernel: about this many workgroups per compute unit over the grid,
+// Segment sizing of the ring kernel: about this many workgroups per compute unit over the grid
+// (one: a single generation of long segments; 1, 2, 4, 8, 16 per CU measured 1.276, 1.284, 1.289,
+// 1.315, 1.357 ms on the 4 x 32768 workload),
 // and never fewer than this many tiles per segment (each segment re-reads a window of halo).
-constexpr int kSwaWgPerCu = 4;
+constexpr int kSwaWgPerCu = 1;
 constexpr int kSwaMinTiles = 8;
 
 template <int NB>
