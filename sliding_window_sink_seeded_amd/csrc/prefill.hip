@@ -133,6 +133,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
 
     const bool skip = MASKED && ((key0 > p0 + kQT - 1) || (key0 + BK - 1 < p0 - a.window + 1) || (p0 >= a.L));
     if (!skip) {
+      // LLVM's interleaving strategy 0 for this scheduling region (K fragment reads spread
+      // between the score MFMAs): -2% on the global layer
+      __builtin_amdgcn_iglp_opt(0);
       const char* sk = smem + (ib & 1) * Tile::kStageBytes;
       const char* sv = sk + Tile::kKBytes;
 
