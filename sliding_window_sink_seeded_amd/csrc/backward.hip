@@ -233,10 +233,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
 
 // ---------------------------------------------------------------------------------- dK/dV kernel
 
-// LDS operand reads of the dK/dV step are issued this many MFMAs ahead of their products (one
-// wave per SIMD cannot hide an LDS round trip behind another wave's work).
-constexpr int kDkdvReadAhead = 6;
-
 // LDS stage of one step: Q rows [32][kQS], dO rows [32][kOS], then lse * log2(e) [32] and D [32].
 // Row strides are padded so that both the 16-byte row reads and the transposing reads of the MFMA
 // operands spread over the banks.
@@ -439,22 +435,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
         acck[t] = mma(f, dsf, (first && ks == 0) ? zero16() : acck[t]);
       }
     }
-    // Issue order: LDS operand reads run kDkdvReadAhead MFMAs ahead. Phase 1: 20 row reads for 20
-    // MFMAs; phase 2: 40 transposing reads (two per fragment) for 20 MFMAs.
-    __builtin_amdgcn_sched_group_barrier(0x100, kDkdvReadAhead, 0);
-#pragma unroll
-    for (int i = 0; i < 20 - kDkdvReadAhead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kDkdvReadAhead, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDkdvReadAhead, 0);
-#pragma unroll
-    for (int i = 0; i < 20 - kDkdvReadAhead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kDkdvReadAhead, 0);
+    // Issue order: LLVM's interleaving strategy 0 spreads the LDS operand reads between the MFMAs
+    // (one wave per SIMD cannot hide an LDS round trip behind another wave's work); it beat
+    // explicit scheduling groups with the reads six MFMAs ahead by 3% on the global layer.
+    __builtin_amdgcn_iglp_opt(0);
   };
 
   // Step 0 is peeled so that the accumulators start as MFMA results. The scheduling barriers
