@@ -46,7 +46,7 @@ typedef enum { MIMO_F32 = 0, MIMO_BF16 = 1 } mimo_dtype;
 enum {
   MIMO_OK = 0,
   MIMO_EINVAL = -1,      /* a size, pointer, alignment, head map or window argument is invalid */
-  MIMO_EUNSUPPORTED = -2, /* valid request that this build does not implement (dtype/dims)       */
+  MIMO_EUNSUPPORTED = -2, /* valid request that the library does not implement (dtype/dims)    */
   MIMO_EWORKSPACE = -3,  /* workspace missing or smaller than the size query returned            */
   MIMO_EHIP = -4         /* the HIP runtime refused a launch                                      */
 };

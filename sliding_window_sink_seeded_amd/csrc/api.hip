@@ -61,7 +61,7 @@ int check_common(int dt, int B, int Hq, int Hkv, int d_qk, int d_v, int window, 
   // for a positive scale
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(MIMO_EINVAL, "scale must be finite and > 0");
   if (d_qk != 192 || d_v != 128)
-    return fail(MIMO_EUNSUPPORTED, "head dims (%d, %d) unsupported; this build has (192, 128)", d_qk, d_v);
+    return fail(MIMO_EUNSUPPORTED, "head dims (%d, %d) unsupported; the library supports (192, 128)", d_qk, d_v);
   return MIMO_OK;
 }
 
@@ -107,7 +107,7 @@ int prefill_impl(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v
 
 int check_rope(const float* table, int positions, int rot_dims, long long need) {
   if (rot_dims != mimo::kRopeDims)
-    return fail(MIMO_EUNSUPPORTED, "rot_dims %d unsupported; this build rotates %d dims", rot_dims,
+    return fail(MIMO_EUNSUPPORTED, "rot_dims %d unsupported; the library rotates %d dims", rot_dims,
                 mimo::kRopeDims);
   if (!table || !aligned16(table)) return fail(MIMO_EINVAL, "rope_table must be non-NULL and 16-byte aligned");
   if (positions < need)
@@ -147,7 +147,7 @@ int mimo_attn_cache_append(mimo_dtype dt, int B, int T, int Hkv, int d_qk, int d
   if (B < 1 || Hkv < 1) return fail(MIMO_EINVAL, "B and Hkv must be >= 1");
   if (T < 1 || T > mimo::kMaxNew) return fail(MIMO_EINVAL, "T must be in 1..%d (got %d)", mimo::kMaxNew, T);
   if (d_qk != 192 || d_v != 128)
-    return fail(MIMO_EUNSUPPORTED, "head dims (%d, %d) unsupported; this build has (192, 128)", d_qk, d_v);
+    return fail(MIMO_EUNSUPPORTED, "head dims (%d, %d) unsupported; the library supports (192, 128)", d_qk, d_v);
   if (C < 1) return fail(MIMO_EINVAL, "C must be >= 1");
   if (max_cache_len < 0 || max_cache_len > (1 << 30) - 8)
     return fail(MIMO_EINVAL, "max_cache_len %d outside [0, 2^30 - 8]", max_cache_len);
@@ -219,7 +219,7 @@ int mimo_attn_prefill_backward(mimo_dtype dt, int B, int L, int Hq, int Hkv, int
 int mimo_attn_rope_table(int n_pos, int rot_dims, double base, float* table, hipStream_t stream) {
   g_err.clear();
   if (rot_dims != mimo::kRopeDims)
-    return fail(MIMO_EUNSUPPORTED, "rot_dims %d unsupported; this build rotates %d dims", rot_dims,
+    return fail(MIMO_EUNSUPPORTED, "rot_dims %d unsupported; the library rotates %d dims", rot_dims,
                 mimo::kRopeDims);
   if (n_pos < 1 || n_pos > (1 << 30)) return fail(MIMO_EINVAL, "n_pos %d outside [1, 2^30]", n_pos);
   if (!std::isfinite(base) || !(base > 1.0)) return fail(MIMO_EINVAL, "base must be finite and > 1");

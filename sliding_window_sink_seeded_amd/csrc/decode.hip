@@ -515,7 +515,7 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
     const float scale_w = fast_exp2(m[cb] - M_use);
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
-      if (rr) __syncthreads();  // round 0 reads are done
+      if (rr) __syncthreads();  // the first pass's reads are done
 #pragma unroll
       for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
