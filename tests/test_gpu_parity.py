@@ -208,6 +208,18 @@ def test_decode_global_short_cache(T):
     check_decode(inp, 128)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,T", [(4, 64, 4, 4), (3, 64, 4, 4), (3, 64, 4, 2), (3, 24, 3, 8), (2, 64, 8, 8)])
+def test_decode_window_column_chunks(B, Hq, Hkv, T):
+    # more than 32 query columns per KV head in one pass: 32-column chunks of the one-pass window
+    # kernel, remapped onto one XCD when the (sequence, KV head) pairs come in whole eights
+    # (B*Hkv = 16, 16) and in launch order otherwise (12, 9)
+    say(f"decode window chunks B={B} {Hq}/{Hkv} T={T}")
+    lens = np.array([0, 33, 127, 128, 4000][:B] + [300] * max(0, B - 5), np.int32)
+    inp = decode_inputs(38 + T + B, B, T, Hq, Hkv, 192, 128, 128, 128, "bf16", len_range=(0, 1))
+    inp.cache_len = lens
+    check_decode(inp, int(lens.max()))
+
+
 def test_decode_ring_one_pass_equals_split():
     say("decode ring: one pass vs two splits")
     inp = decode_inputs(37, 6, 4, 64, 8, 192, 128, 128, 128, "bf16", len_range=(0, 3000))

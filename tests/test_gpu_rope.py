@@ -113,6 +113,19 @@ def test_decode_rope_ring(dtype, T):
     check_lse(lse, ref_lse, dtype)
 
 
+@pytest.mark.parametrize("B", [3, 4])
+def test_decode_rope_ring_column_chunks(B):
+    # 16 query heads per KV head x 4 tokens = 64 columns: the RoPE instance of the one-pass window
+    # kernel in 32-column chunks (rotation positions follow each chunk's columns)
+    say(f"decode rope ring, column chunks, B={B}")
+    lens = np.array([0, 127, 900, 5000][:B], np.int32)
+    inp = decode_inputs(49 + B, B, 4, 64, 4, 192, 128, 128, 128, "bf16", len_range=(0, 1))
+    inp.cache_len = lens
+    o, lse, ref_o, ref_lse = run_decode_rope(inp, int(lens.max()), BASES["swa"])
+    assert_output_close(o, ref_o, "bf16")
+    check_lse(lse, ref_lse, "bf16")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("num_splits", [1, 3])
 def test_decode_rope_global(dtype, num_splits):
