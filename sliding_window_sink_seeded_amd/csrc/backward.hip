@@ -293,9 +293,26 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   // workgroups start at the last tile of the sequence, so the ones running together read the
   // same Q / dO rows at about the same time and share them through L2 (head-major order made
   // each workgroup walk its own tiles and re-read Q / dO from HBM).
+  //
+  // Short windows (at most 32 NW + 1 keys): key block kb + 1 sees the tiles from split =
+  // qt0 + 32 NW / kQT on, which kb sees as its upper half. In one descending order the two reach
+  // those tiles half a walk apart and each fetches them from beyond L2. Instead even blocks walk
+  // their upper half first and odd blocks their lower half first (each half descending), so two
+  // neighbours dispatched together read every shared tile in the same step. Interior (mask-free)
+  // tiles do not exist for such windows.
   const int qt_last = last_q / kQT;
+  const int split = qt0 + 32 * NW / kQT;
+  const bool alt = a.window <= 32 * NW + 1 && qt_last >= split;
+  const bool odd = kb & 1;
+  const int n_first = odd ? split - qt0 : qt_last - split + 1;
   auto step_head = [&](int step) { return step % a.G; };
-  auto step_row = [&](int step) { return (qt_last - step / a.G) * kQT; };
+  auto step_row = [&](int step) {
+    const int t = step / a.G;
+    if (!alt) return (qt_last - t) * kQT;
+    if (t < n_first) return (odd ? split - 1 - t : qt_last - t) * kQT;
+    const int u = t - n_first;
+    return (odd ? qt_last - u : split - 1 - u) * kQT;
+  };
 
   // staging: thread tid moves row tid / 8 of the step's Q and dO tiles; threads 0..63 also move
   // lse (rows 0..31) and D (rows 32..63 -> D of row tid - 32)
@@ -447,12 +464,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   //
   // Steps whose tile every key of the workgroup sees in full need no mask: rows at or after the
   // block's last key (q0 >= kb0 + 32 NW - 1), inside the window of its first key, and before L.
-  // In the descending order they form one run [s_a, s_b); the steps before (a partial last tile)
-  // and after it (the tiles on the diagonal) take the masked variant. Each loop stays free of
-  // branches.
+  // In the descending order (long windows) they form one run [s_a, s_b); the steps before (a
+  // partial last tile) and after it (the tiles on the diagonal) take the masked variant. Each loop
+  // stays free of branches.
   auto stage = [&](int step) { return smem + (step & 1) * St::kBytes; };
   int s_a = 0, s_b = 0;
-  {
+  if (!alt) {
     // tile t is interior iff 32 t >= kb0 + 32 NW - 1, 32 t <= kb0 + W - 32 and 32 t <= L - 32
     const int t_lo = (kb0 + 32 * NW - 1 + kQT - 1) / kQT;
     const long long lim = min((long long)kb0 + a.window - kQT, (long long)a.L - kQT);
