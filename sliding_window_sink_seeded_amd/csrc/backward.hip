@@ -246,14 +246,20 @@ struct DkdvStage {
   static_assert(kQBytes % 16 == 0 && kOBytes % 16 == 0, "16-byte aligned rows");
 };
 
+// dK/dV: windows up to this many keys run two-wave workgroups (see the launcher); the group-phase
+// tile order (see the kernel) applies while a key block sees at most kDkdvMaxGroups tile groups.
+constexpr int kDkdvShortWindow = 256;
+constexpr int kDkdvMaxGroups = 8;
+
 template <typename E, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a) {
   using Frag = typename E::Frag;
   using St = DkdvStage<E>;
   constexpr int NT = NW * 64;
-  static_assert(NT == 256, "staging assumes 8 threads per staged row");
-  constexpr int QPT = kDQK * E::kBytes / 16 / 8;  // 16-byte Q chunks per thread
-  constexpr int OPT = kDV * E::kBytes / 16 / 8;   // 16-byte dO chunks per thread
+  static_assert(NT == 128 || NT == 256, "staging: 8 threads per staged row, 1 or 2 rows each");
+  constexpr int RPT = 256 / NT;                   // staged rows per thread
+  constexpr int QPT = kDQK * E::kBytes / 16 / 8;  // 16-byte Q chunks per thread and row
+  constexpr int OPT = kDV * E::kBytes / 16 / 8;   // 16-byte dO chunks per thread and row
   __shared__ __attribute__((aligned(16))) char smem[2 * St::kBytes];
 
   const int tid = threadIdx.x;
@@ -288,52 +294,57 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   const int last_q = min(a.L - 1, kb0 + 32 * NW - 1 + a.window - 1);
   const int qt0 = kb0 / kQT;
   const int ntiles = last_q / kQT - qt0 + 1;
-  const int nsteps = a.G * ntiles;
   // Step order: tile-major from the last query tile down, every head of a tile in turn. All
   // workgroups start at the last tile of the sequence, so the ones running together read the
   // same Q / dO rows at about the same time and share them through L2 (head-major order made
   // each workgroup walk its own tiles and re-read Q / dO from HBM).
   //
-  // Short windows (at most 32 NW + 1 keys): key block kb + 1 sees the tiles from split =
-  // qt0 + 32 NW / kQT on, which kb sees as its upper half. In one descending order the two reach
-  // those tiles half a walk apart and each fetches them from beyond L2. Instead even blocks walk
-  // their upper half first and odd blocks their lower half first (each half descending), so two
-  // neighbours dispatched together read every shared tile in the same step. Interior (mask-free)
-  // tiles do not exist for such windows.
+  // Short windows: the tiles form groups of GS = 32 NW / kQT (the rows of one key block); block kb
+  // sees groups kb .. kb + ng - 1 and shares each with the ng - 1 blocks beside it. In one
+  // descending order the sharers reach a group at different moments and each fetches it from
+  // beyond L2. Instead every block walks its groups in the order of m mod ng (each group's tiles
+  // descending), so the ng blocks that share group m, dispatched together, read its tiles in the
+  // same steps. Blocks at the end of the sequence also walk the tiles past L (masked rows, clamped
+  // loads), which keeps their phases aligned with their neighbours'. Interior (mask-free) tiles do
+  // not exist for such windows.
   const int qt_last = last_q / kQT;
-  const int split = qt0 + 32 * NW / kQT;
-  const bool alt = a.window <= 32 * NW + 1 && qt_last >= split;
-  const bool odd = kb & 1;
-  const int n_first = odd ? split - qt0 : qt_last - split + 1;
+  constexpr int GS = 32 * NW / kQT;
+  const int ng = (kb0 + 32 * NW - 1 + a.window - 1) / kQT / GS - kb + 1;  // window <= L
+  const bool alt = ng <= kDkdvMaxGroups;
+  const int kbm = kb % ng;
+  const int nsteps = a.G * (alt ? ng * GS : ntiles);
   auto step_head = [&](int step) { return step % a.G; };
   auto step_row = [&](int step) {
     const int t = step / a.G;
     if (!alt) return (qt_last - t) * kQT;
-    if (t < n_first) return (odd ? split - 1 - t : qt_last - t) * kQT;
-    const int u = t - n_first;
-    return (odd ? qt_last - u : split - 1 - u) * kQT;
+    const int ph = t / GS - kbm;
+    const int m = kb + (ph < 0 ? ph + ng : ph);
+    return (m * GS + GS - 1 - t % GS) * kQT;
   };
 
-  // staging: thread tid moves row tid / 8 of the step's Q and dO tiles; threads 0..63 also move
-  // lse (rows 0..31) and D (rows 32..63 -> D of row tid - 32)
+  // staging: thread tid moves rows tid / 8 + NT / 8 * r (r < RPT) of the step's Q and dO tiles;
+  // threads 0..63 also move lse (rows 0..31) and D (rows 32..63 -> D of row tid - 32)
   const int srow = tid >> 3, spart = tid & 7;
   const size_t qrow_stride = (size_t)a.Hq * kDQK * E::kBytes;
   const size_t orow_stride = (size_t)a.Hq * kDV * E::kBytes;
   struct Staged {
-    u32x4 q[QPT], o[OPT];
+    u32x4 q[RPT][QPT], o[RPT][OPT];
     float l;
   };
   auto load_step = [&](int step, Staged& r) {
     const int j = step_head(step);
     const int q0 = step_row(step);
     const int head = a.hl.at(g * a.G + j);
-    const int qrow = min(q0 + srow, a.L - 1);
-    const char* qp = (const char*)a.q + ((size_t)b * a.L + qrow) * qrow_stride + (size_t)head * kDQK * E::kBytes;
-    const char* op = (const char*)a.d_o + ((size_t)b * a.L + qrow) * orow_stride + (size_t)head * kDV * E::kBytes;
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) r.q[i] = ld16(qp + 16 * (spart * QPT + i));
+    for (int rr = 0; rr < RPT; ++rr) {
+      const int qrow = min(q0 + srow + NT / 8 * rr, a.L - 1);
+      const char* qp = (const char*)a.q + ((size_t)b * a.L + qrow) * qrow_stride + (size_t)head * kDQK * E::kBytes;
+      const char* op = (const char*)a.d_o + ((size_t)b * a.L + qrow) * orow_stride + (size_t)head * kDV * E::kBytes;
 #pragma unroll
-    for (int i = 0; i < OPT; ++i) r.o[i] = ld16(op + 16 * (spart * OPT + i));
+      for (int i = 0; i < QPT; ++i) r.q[rr][i] = ld16(qp + 16 * (spart * QPT + i));
+#pragma unroll
+      for (int i = 0; i < OPT; ++i) r.o[rr][i] = ld16(op + 16 * (spart * OPT + i));
+    }
     {  // every thread loads (threads past 64 re-read a D entry): no branch and no use of the
        // value before store_step, so nothing waits for this load here
       const int rr = min(q0 + (tid & 31), a.L - 1);
@@ -342,12 +353,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
     }
   };
   auto store_step = [&](char* stage, const Staged& r) {
-    char* sq = stage + (srow * St::kQS + spart * QPT * (16 / E::kBytes)) * E::kBytes;
-    char* so = stage + St::kQBytes + (srow * St::kOS + spart * OPT * (16 / E::kBytes)) * E::kBytes;
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) st16(sq + 16 * i, r.q[i]);
+    for (int rr = 0; rr < RPT; ++rr) {
+      const int row = srow + NT / 8 * rr;
+      char* sq = stage + (row * St::kQS + spart * QPT * (16 / E::kBytes)) * E::kBytes;
+      char* so = stage + St::kQBytes + (row * St::kOS + spart * OPT * (16 / E::kBytes)) * E::kBytes;
 #pragma unroll
-    for (int i = 0; i < OPT; ++i) st16(so + 16 * i, r.o[i]);
+      for (int i = 0; i < QPT; ++i) st16(sq + 16 * i, r.q[rr][i]);
+#pragma unroll
+      for (int i = 0; i < OPT; ++i) st16(so + 16 * i, r.o[rr][i]);
+    }
     if (tid < 2 * kQT)
       reinterpret_cast<float*>(stage + St::kQBytes + St::kOBytes)[tid] = tid < kQT ? r.l * kLog2e : r.l;
   };
@@ -542,23 +557,32 @@ size_t backward_ws_bytes(int B, int L, int Hq) {
   return backward_ws_d_bytes(B, L, Hq) + (size_t)Hq * B * n_qtiles * 4;
 }
 
+
 template <typename E>
 static hipError_t launch_backward(BackwardArgs a, hipStream_t stream) {
-  constexpr int NW = 8, BK = 32, NWK = 4;
+  constexpr int NW = 8, BK = 32;
+  // dK/dV workgroups of 4 waves (128 keys) walk every query tile that sees any of their keys; under
+  // a short window each wave sees only some of them (5 of 8 at W = 128) and computes the rest with
+  // p = 0. Two-wave workgroups (64 keys, two per CU) walk 6 tiles for the same 5.
+  const bool kv2 = a.window <= kDkdvShortWindow;
+  const int nwk = kv2 ? 2 : 4;
   int hg = 1;
   while (hg < NW && a.G % (hg * 2) == 0) hg *= 2;
   a.heads_per_wg = hg;
   a.n_hchunks = a.G / hg;
   const int rows_per_wg = kQT * (NW / hg);
   a.n_qblocks = (a.L + rows_per_wg - 1) / rows_per_wg;
-  a.n_kblocks = (a.L + 32 * NWK - 1) / (32 * NWK);
+  a.n_kblocks = (a.L + 32 * nwk - 1) / (32 * nwk);
   a.n_qtiles = (a.L + kQT - 1) / kQT;
 
   const long long n_dq = (long long)a.n_qblocks * a.B * a.Hkv * a.n_hchunks;
   const long long n_kv = (long long)a.n_kblocks * a.B * a.Hkv;
   if (n_dq > 0x7fffffffLL || n_kv > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((bwd_dq_kernel<E, NW, BK>), dim3((unsigned)n_dq), dim3(NW * 64), 0, stream, a);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, NWK>), dim3((unsigned)n_kv), dim3(NWK * 64), 0, stream, a);
+  if (kv2)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, 2>), dim3((unsigned)n_kv), dim3(128), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, 4>), dim3((unsigned)n_kv), dim3(256), 0, stream, a);
   if (a.dsink) hipLaunchKernelGGL(bwd_sink_kernel, dim3(a.Hq), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
