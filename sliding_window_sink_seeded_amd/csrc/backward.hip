@@ -410,7 +410,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   // dV / dK contributions. A wave none of whose keys the tile sees computes with p = 0 (no
   // branch: branches inside the loop make the compiler move the accumulators between register
   // files on every step).
-  auto compute = [&](int step, bool first, auto masked) {
+  // (forced inline: the fp32 instance was otherwise called with a 2.3 KB stack frame)
+  auto compute = [&](int step, bool first, auto masked) __attribute__((always_inline)) {
     const int q0 = step_row(step);
     const bool active = (kw0 < a.L) && (q0 + kQT - 1 >= kw0) && (q0 <= kw0 + 31 + a.window - 1);
     const unsigned wlim = active ? (unsigned)a.window : 0u;  // no visible key when inactive
@@ -563,8 +564,9 @@ static hipError_t launch_backward(BackwardArgs a, hipStream_t stream) {
   constexpr int NW = 8, BK = 32;
   // dK/dV workgroups of 4 waves (128 keys) walk every query tile that sees any of their keys; under
   // a short window each wave sees only some of them (5 of 8 at W = 128) and computes the rest with
-  // p = 0. Two-wave workgroups (64 keys, two per CU) walk 6 tiles for the same 5.
-  const bool kv2 = a.window <= kDkdvShortWindow;
+  // p = 0. Two-wave workgroups (64 keys, two per CU) walk 6 tiles for the same 5 (bf16; the fp32
+  // kernel's doubled staging registers would spill).
+  const bool kv2 = E::kBytes == 2 && a.window <= kDkdvShortWindow;
   const int nwk = kv2 ? 2 : 4;
   int hg = 1;
   while (hg < NW && a.G % (hg * 2) == 0) hg *= 2;
@@ -579,10 +581,14 @@ static hipError_t launch_backward(BackwardArgs a, hipStream_t stream) {
   const long long n_kv = (long long)a.n_kblocks * a.B * a.Hkv;
   if (n_dq > 0x7fffffffLL || n_kv > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((bwd_dq_kernel<E, NW, BK>), dim3((unsigned)n_dq), dim3(NW * 64), 0, stream, a);
-  if (kv2)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, 2>), dim3((unsigned)n_kv), dim3(128), 0, stream, a);
-  else
+  if constexpr (E::kBytes == 2) {
+    if (kv2)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, 2>), dim3((unsigned)n_kv), dim3(128), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, 4>), dim3((unsigned)n_kv), dim3(256), 0, stream, a);
+  } else {
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, 4>), dim3((unsigned)n_kv), dim3(256), 0, stream, a);
+  }
   if (a.dsink) hipLaunchKernelGGL(bwd_sink_kernel, dim3(a.Hq), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
