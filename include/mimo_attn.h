@@ -134,14 +134,27 @@ int mimo_attn_rope_table(int n_pos, int rot_dims, double base, float* table, hip
  * mimo_attn_prefill for q and k given BEFORE the rotary embedding: every Q and K head vector of row
  * i is rotated by position i with rope_table (rope_positions >= L rows from mimo_attn_rope_table)
  * before the dot products; in bf16 the rotated values are rounded to bf16 (nearest even) first.
+ *
+ * workspace (device, caller-owned, 16-byte aligned) is optional. With NULL, K is rotated as its
+ * blocks are staged, by every workgroup that reads them. With at least
+ * mimo_attn_prefill_rope_workspace_size() bytes, K is rotated once into the workspace (the same
+ * arithmetic, so the same results) and the attention reads it from there; the size is 0 where
+ * the chosen kernel rotates each key once anyway (bf16 sliding windows of at most 129 keys with
+ * a multiple of 8 query heads per KV head), and B * L * Hkv * d_qk elements otherwise. The
+ * workspace contents are scratch: nothing is expected in it and nothing is left for the caller.
+ *
  * Other arguments and errors as mimo_attn_prefill; additionally MIMO_EINVAL for a NULL or
- * misaligned table or rope_positions < L, MIMO_EUNSUPPORTED for rot_dims != 64.
+ * misaligned table, rope_positions < L or a misaligned workspace, MIMO_EWORKSPACE for a
+ * non-NULL workspace smaller than the size query, MIMO_EUNSUPPORTED for rot_dims != 64.
  */
+size_t mimo_attn_prefill_rope_workspace_size(mimo_dtype dt, int B, int L, int Hq, int Hkv,
+                                             int window);
 int mimo_attn_prefill_rope(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v,
                            const void* q, const void* k, const void* v, int window,
                            const float* sink, const int32_t* kv_head_of_q, float scale,
-                           const float* rope_table, int rope_positions, int rot_dims, void* o,
-                           float* lse, hipStream_t stream);
+                           const float* rope_table, int rope_positions, int rot_dims,
+                           void* workspace, size_t workspace_bytes, void* o, float* lse,
+                           hipStream_t stream);
 
 /*
  * mimo_attn_decode for q and k_new given BEFORE the rotary embedding: new token t of sequence b is

@@ -19,13 +19,14 @@ import ctypes
 import math
 import os
 
-__all__ = ["prefill", "decode", "decode_workspace_size", "rope_table", "prefill_backward", "cache_append",
+__all__ = ["prefill", "decode", "decode_workspace_size", "prefill_rope_workspace_size", "rope_table", "prefill_backward", "cache_append",
            "backward_workspace_size", "last_error", "version", "library", "LIB_PATH", "MimoError",
            "EXPORTS", "ROPE_DIMS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmimo_attn.so")
 EXPORTS = ("mimo_attn_prefill", "mimo_attn_decode", "mimo_attn_decode_workspace_size",
-           "mimo_attn_rope_table", "mimo_attn_prefill_rope", "mimo_attn_decode_rope",
+           "mimo_attn_rope_table", "mimo_attn_prefill_rope", "mimo_attn_prefill_rope_workspace_size",
+           "mimo_attn_decode_rope",
            "mimo_attn_prefill_backward", "mimo_attn_prefill_backward_workspace_size",
            "mimo_attn_cache_append",
            "mimo_attn_last_error", "mimo_attn_version")
@@ -64,8 +65,10 @@ def library() -> ctypes.CDLL:
     lib.mimo_attn_rope_table.argtypes = [i32, i32, ctypes.c_double, vp, vp]
     lib.mimo_attn_rope_table.restype = i32
     lib.mimo_attn_prefill_rope.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp,
-                                           vp, f32, vp, i32, i32, vp, vp, vp]
+                                           vp, f32, vp, i32, i32, vp, sz, vp, vp, vp]
     lib.mimo_attn_prefill_rope.restype = i32
+    lib.mimo_attn_prefill_rope_workspace_size.argtypes = [i32] * 6
+    lib.mimo_attn_prefill_rope_workspace_size.restype = sz
     lib.mimo_attn_decode_rope.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                           i32, vp, vp, i32, i32, vp, vp, f32, vp, i32, i32, i32, vp,
                                           sz, vp, vp, vp]
@@ -166,12 +169,15 @@ def _rope_arg(rope):
 
 
 def prefill(q, k, v, window: int, sink=None, scale: float | None = None, kv_map=None, out=None,
-            lse=None, return_lse: bool = False, stream=None, rope=None):
+            lse=None, return_lse: bool = False, stream=None, rope=None, workspace=None,
+            rotate_k_once: bool = True):
     """Sink-seeded windowed prefill. q [B, L, Hq, dqk], k [B, L, Hkv, dqk], v [B, L, Hkv, dv].
 
     window >= L means global causal attention. sink: fp32 [Hq] GPU tensor or None. kv_map: host
     sequence of Hq KV-head indices (None = contiguous groups). rope: None, or a table from
-    rope_table() when q and k are given before the rotary embedding. Returns (o, lse or None).
+    rope_table() when q and k are given before the rotary embedding; then K is rotated once into a
+    workspace (given, or allocated here when the chosen kernel uses one) unless rotate_k_once is
+    False, which rotates each K block as it is staged. Returns (o, lse or None).
     """
     import torch
 
@@ -207,13 +213,30 @@ def prefill(q, k, v, window: int, sink=None, scale: float | None = None, kv_map=
                                          _ptr(lse), _stream(stream))
     else:
         n_pos = _rope_arg(rope)
+        ws_have = 0
+        if not rotate_k_once:
+            workspace = None
+        elif workspace is None:
+            need = prefill_rope_workspace_size(q.dtype, B, L, Hq, Hkv, window)
+            if need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            ws_have = workspace.numel() * workspace.element_size()
         rc = library().mimo_attn_prefill_rope(dt, B, L, Hq, Hkv, dqk, dv, _ptr(q), _ptr(k), _ptr(v),
                                               int(window), _ptr(sink), kvm, float(scale), _ptr(rope),
-                                              int(n_pos), ROPE_DIMS, _ptr(out), _ptr(lse),
-                                              _stream(stream))
+                                              int(n_pos), ROPE_DIMS, _ptr(workspace), ws_have,
+                                              _ptr(out), _ptr(lse), _stream(stream))
     del keep
     _check(rc)
     return out, lse
+
+
+def prefill_rope_workspace_size(dtype, B: int, L: int, Hq: int, Hkv: int, window: int) -> int:
+    """Bytes with which a RoPE prefill rotates K once (0: the chosen kernel has no use for them)."""
+    import torch
+
+    code = MIMO_BF16 if dtype in (torch.bfloat16, "bf16") else MIMO_F32
+    return int(library().mimo_attn_prefill_rope_workspace_size(code, B, L, Hq, Hkv, int(window)))
 
 
 def decode_workspace_size(B, T, Hq, Hkv, dv, max_cache_len, window, num_splits=0) -> int:

@@ -80,8 +80,8 @@ namespace {
 // rope: NULL, or a table of at least L positions for Q/K given before the rotary embedding
 int prefill_impl(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v, const void* q,
                  const void* k, const void* v, int window, const float* sink,
-                 const int32_t* kv_head_of_q, float scale, const float* rope, void* o, float* lse,
-                 hipStream_t stream) {
+                 const int32_t* kv_head_of_q, float scale, const float* rope, void* k_ws, void* o,
+                 float* lse, hipStream_t stream) {
   g_err.clear();
   if (int rc = check_common(dt, B, Hq, Hkv, d_qk, d_v, window, scale)) return rc;
   if (L < 1) return fail(MIMO_EINVAL, "L must be >= 1");
@@ -95,7 +95,7 @@ int prefill_impl(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v
   if ((double)B * L * Hq * d_qk * elem > 4.6e18) return fail(MIMO_EINVAL, "tensor too large");
 
   mimo::PrefillArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.sink = sink; a.rope = rope;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.sink = sink; a.rope = rope; a.k_ws = k_ws;
   a.B = B; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
   a.window = window < L ? window : L;
   a.scale_log2 = scale * mimo::kLog2e;
@@ -124,18 +124,35 @@ int mimo_attn_prefill(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, in
                       const int32_t* kv_head_of_q, float scale, void* o, float* lse,
                       hipStream_t stream) {
   return prefill_impl(dt, B, L, Hq, Hkv, d_qk, d_v, q, k, v, window, sink, kv_head_of_q, scale,
-                      nullptr, o, lse, stream);
+                      nullptr, nullptr, o, lse, stream);
+}
+
+size_t mimo_attn_prefill_rope_workspace_size(mimo_dtype dt, int B, int L, int Hq, int Hkv,
+                                             int window) {
+  if ((dt != MIMO_BF16 && dt != MIMO_F32) || B < 1 || L < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv ||
+      window < 1)
+    return 0;
+  return mimo::prefill_rope_ws_bytes(dt == MIMO_BF16, B, L, Hq, Hkv, window);
 }
 
 int mimo_attn_prefill_rope(mimo_dtype dt, int B, int L, int Hq, int Hkv, int d_qk, int d_v,
                            const void* q, const void* k, const void* v, int window,
                            const float* sink, const int32_t* kv_head_of_q, float scale,
-                           const float* rope_table, int rope_positions, int rot_dims, void* o,
-                           float* lse, hipStream_t stream) {
+                           const float* rope_table, int rope_positions, int rot_dims,
+                           void* workspace, size_t workspace_bytes, void* o, float* lse,
+                           hipStream_t stream) {
   g_err.clear();
   if (int rc = check_rope(rope_table, rope_positions, rot_dims, L)) return rc;
+  void* k_ws = nullptr;
+  if (workspace) {
+    if (!aligned16(workspace)) return fail(MIMO_EINVAL, "workspace must be 16-byte aligned");
+    const size_t need = mimo_attn_prefill_rope_workspace_size(dt, B, L, Hq, Hkv, window);
+    if (workspace_bytes < need)
+      return fail(MIMO_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (need > 0) k_ws = workspace;
+  }
   return prefill_impl(dt, B, L, Hq, Hkv, d_qk, d_v, q, k, v, window, sink, kv_head_of_q, scale,
-                      rope_table, o, lse, stream);
+                      rope_table, k_ws, o, lse, stream);
 }
 
 int mimo_attn_cache_append(mimo_dtype dt, int B, int T, int Hkv, int d_qk, int d_v,

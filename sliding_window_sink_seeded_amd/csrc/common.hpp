@@ -212,7 +212,8 @@ constexpr int kRopeDims = 64;
 
 // cs[2j], cs[2j+1] = cos, sin for element j of `lo`; lo holds dims i0.., hi the partner dims
 // i0 + 32..; bf16 chunks carry 8 elements, fp32 chunks 4. Rotated values are rounded back to the
-// storage type (bf16: round to nearest even).
+// storage type (bf16: round to nearest even). The fused multiply-adds are written out so that every
+// kernel that inlines this rounds the same way (left to the compiler, contraction varied by kernel).
 template <typename E>
 __device__ __forceinline__ void rope_rotate_chunk(u32x4& lo, u32x4& hi, const float* cs) {
   if constexpr (E::kBytes == 2) {
@@ -221,16 +222,16 @@ __device__ __forceinline__ void rope_rotate_chunk(u32x4& lo, u32x4& hi, const fl
       const float x0 = __uint_as_float(lo[w] << 16), x1 = __uint_as_float(lo[w] & 0xFFFF0000u);
       const float y0 = __uint_as_float(hi[w] << 16), y1 = __uint_as_float(hi[w] & 0xFFFF0000u);
       const float c0 = cs[4 * w], s0 = cs[4 * w + 1], c1 = cs[4 * w + 2], s1 = cs[4 * w + 3];
-      lo[w] = pack_bf16x2(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
-      hi[w] = pack_bf16x2(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+      lo[w] = pack_bf16x2(__builtin_fmaf(x0, c0, -(y0 * s0)), __builtin_fmaf(x1, c1, -(y1 * s1)));
+      hi[w] = pack_bf16x2(__builtin_fmaf(y0, c0, x0 * s0), __builtin_fmaf(y1, c1, x1 * s1));
     }
   } else {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float x = __uint_as_float(lo[w]), y = __uint_as_float(hi[w]);
       const float c = cs[2 * w], s = cs[2 * w + 1];
-      lo[w] = __float_as_uint(x * c - y * s);
-      hi[w] = __float_as_uint(y * c + x * s);
+      lo[w] = __float_as_uint(__builtin_fmaf(x, c, -(y * s)));
+      hi[w] = __float_as_uint(__builtin_fmaf(y, c, x * s));
     }
   }
 }
@@ -258,8 +259,8 @@ __device__ __forceinline__ void rope_rotate_frag(F& lo, F& hi, const float (&cs)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = lo[e], y = hi[e], c = cs[2 * e], s = cs[2 * e + 1];
-      lo[e] = x * c - y * s;
-      hi[e] = y * c + x * s;
+      lo[e] = __builtin_fmaf(x, c, -(y * s));
+      hi[e] = __builtin_fmaf(y, c, x * s);
     }
   }
 }

@@ -25,6 +25,7 @@ struct PrefillArgs {
   int n_segments;    // sliding-window ring kernel: segments of consecutive tiles per (b, g, chunk)
   int tiles_per_wg;  // sliding-window ring kernel: 32-row tiles per segment
   const float* rope;  // [>= L][32][2] (cos, sin) when Q/K arrive before the rotary embedding, else NULL
+  void* k_ws;         // with rope: room for the rotated K ([B, L, Hkv, 192]), or NULL
   HeadList hl;
 };
 
@@ -97,6 +98,9 @@ struct AppendArgs {
 hipError_t rope_table_launch(int n_pos, double base, float* table, hipStream_t stream);
 // Picks the prefill variant (fills the tiling fields of `a`) and launches it on `stream`.
 hipError_t prefill_launch(bool bf16, PrefillArgs a, hipStream_t stream);
+// Bytes of k_ws with which prefill_launch rotates K once instead of at every staging (0: the
+// chosen kernel has no use for it).
+size_t prefill_rope_ws_bytes(bool bf16, int B, int L, int Hq, int Hkv, int window);
 // Launches the decode kernel and, when a.nsplit > 1, the combine kernel on `stream`.
 hipError_t decode_launch(bool bf16, const DecodeArgs& a, hipStream_t stream);
 // Launches the dq, dk/dv and sink-gradient kernels on `stream` (a.D / a.sink_part point into the

@@ -35,7 +35,11 @@ namespace mimo {
 
 constexpr float kLazyRescale = 8.f;  // log2 units
 
-template <typename E, int NW, int BK, bool ROPE>
+// ROPE: kPreRopeNone (Q and K rotated already), kPreRopeQK (both rotated here: Q once, K at every
+// staging), kPreRopeQ (Q rotated here, K rotated beforehand by rope_k_kernel).
+constexpr int kPreRopeNone = 0, kPreRopeQK = 1, kPreRopeQ = 2;
+
+template <typename E, int NW, int BK, int ROPE>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   using Tile = PrefillTile<E, BK>;
   using Frag = typename E::Frag;
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
     const char* qrow = (const char*)a.q + (((size_t)b * a.L + qload) * a.Hq + head) * kDQK * E::kBytes;
 #pragma unroll
     for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
-    if constexpr (ROPE) {
+    if constexpr (ROPE != kPreRopeNone) {
       // fragments 0, 1 hold dims 16 kk + 8 half .. +7 of the rotated slice, 2, 3 their partners
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -102,8 +106,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
 
   // bf16 64-key blocks go global -> LDS directly (no staging registers); the others through
   // registers
-  constexpr bool kDMA = E::kBytes == 2 && BK == 64 && !ROPE;
-  KVStager<E, NT, BK, ROPE ? kRopeMem : kRopeNone> st;
+  constexpr bool kDMA = E::kBytes == 2 && BK == 64 && ROPE != kPreRopeQK;
+  KVStager<E, NT, BK, ROPE == kPreRopeQK ? kRopeMem : kRopeNone> st;
   KVStagerDMA<NW, 64> dma;  // used only when kDMA (BK == 64)
   if constexpr (kDMA) {
     dma.init(krow_stride, vrow_stride, wave, lane);
@@ -469,14 +473,48 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   }
 }
 
+// K [B, L, Hkv, 192] -> k_ws with the leading 64 dims of row l rotated by position l: one thread
+// per 16-byte chunk; a thread of a chunk in the first 32 dims rotates it together with its
+// partner 32 dims on (the same arithmetic as the rotation at staging), chunks past 64 are copied.
+template <typename E>
+__global__ __launch_bounds__(256) void rope_k_kernel(const PrefillArgs a) {
+  constexpr int NCH = kDQK / E::kPerChunk;        // chunks per row
+  constexpr int H = kRopeDims / 2 / E::kPerChunk;  // chunks in 32 dims
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)a.B * a.L * a.Hkv * NCH) return;
+  const int c = (int)(idx % NCH);
+  const long long row = idx / NCH;                 // (b * L + l) * Hkv + g
+  const int l = (int)((row / a.Hkv) % a.L);
+  const char* src = (const char*)a.k + row * kDQK * E::kBytes;
+  char* dst = (char*)a.k_ws + row * kDQK * E::kBytes;
+  if (c < H) {
+    u32x4 lo = ld16(src + 16 * c), hi = ld16(src + 16 * (c + H));
+    float cs[2 * E::kPerChunk];
+    rope_load<E::kPerChunk>(a.rope, l, c * E::kPerChunk, cs);
+    rope_rotate_chunk<E>(lo, hi, cs);
+    st16(dst + 16 * c, lo);
+    st16(dst + 16 * (c + H), hi);
+  } else if (c >= 2 * H) {
+    st16(dst + 16 * c, ld16(src + 16 * c));
+  }
+}
+
 template <typename E, int NW, int BK>
 static hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const long long n_wg = (long long)a.n_qblocks * a.B * a.Hkv * a.n_hchunks;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (a.rope)
-    hipLaunchKernelGGL((prefill_kernel<E, NW, BK, true>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<E, NW, BK, false>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, a);
+  if (a.rope && a.k_ws) {
+    // rotate K once into k_ws; the attention then rotates only Q and stages K as without RoPE
+    const long long units = (long long)a.B * a.L * a.Hkv * (kDQK / E::kPerChunk);
+    hipLaunchKernelGGL(rope_k_kernel<E>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, a);
+    PrefillArgs r = a;
+    r.k = a.k_ws;
+    hipLaunchKernelGGL((prefill_kernel<E, NW, BK, kPreRopeQ>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, r);
+  } else if (a.rope) {
+    hipLaunchKernelGGL((prefill_kernel<E, NW, BK, kPreRopeQK>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<E, NW, BK, kPreRopeNone>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -564,6 +602,16 @@ hipError_t prefill_launch(bool bf16, PrefillArgs a, hipStream_t stream) {
   }
   if (global) return launch<BF16, NW, 64>(a, stream);
   return launch<BF16, NW, 32>(a, stream);
+}
+
+size_t prefill_rope_ws_bytes(bool bf16, int B, int L, int Hq, int Hkv, int window) {
+  constexpr int NW = 8;
+  const int G = Hq / Hkv;
+  int hg = 1;
+  while (hg < NW && G % (hg * 2) == 0) hg *= 2;
+  const int w = window < L ? window : L;
+  if (bf16 && w < L && hg == NW && w <= 129) return 0;  // the ring kernel rotates K once per segment
+  return (size_t)B * L * Hkv * kDQK * (bf16 ? 2 : 4);
 }
 
 }  // namespace mimo

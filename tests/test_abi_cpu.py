@@ -174,7 +174,8 @@ def prefill_rope(lib, table=P, positions=64, rot=64, L=64, **kw):
     a.update(kw)
     return lib.mimo_attn_prefill_rope(a["dt"], a["B"], L, a["Hq"], a["Hkv"], a["dqk"], a["dv"],
                                       a["q"], a["k"], a["v"], a["window"], a["sink"], a["kvm"],
-                                      a["scale"], table, positions, rot, a["o"], a["lse"], None)
+                                      a["scale"], table, positions, rot, a.get("ws"), a.get("ws_bytes", 0),
+                                      a["o"], a["lse"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -184,6 +185,8 @@ def prefill_rope(lib, table=P, positions=64, rot=64, L=64, **kw):
     (dict(rot=128), EUNSUPPORTED),
     (dict(B=0), EINVAL),                   # the plain prefill checks still apply
     (dict(scale=0.0), EINVAL),
+    (dict(ws=P_MIS, ws_bytes=1 << 30, window=10**6), EINVAL),      # misaligned workspace
+    (dict(ws=P, ws_bytes=100, window=10**6), EWORKSPACE),           # global layer: too small
 ])
 def test_prefill_rope_validation(lib, kw, code):
     assert prefill_rope(lib, **kw) == code
@@ -275,3 +278,17 @@ def append(lib, dt=BF16, B=2, T=4, Hkv=8, dqk=192, dv=128, kn=P, vn=P, kc=P, vc=
 def test_cache_append_validation(lib, kw, code):
     assert append(lib, **kw) == code
     assert mimo.last_error() != ""
+
+
+def test_prefill_rope_workspace_size(lib):
+    f = lib.mimo_attn_prefill_rope_workspace_size
+    f.restype = ctypes.c_size_t
+    # bf16 sliding window with 8 query heads per KV head: the ring kernel rotates K once per segment
+    assert f(BF16, 4, 32768, 64, 8, 128) == 0
+    # the global layer (and fp32, and windows past 129): one rotated copy of K
+    assert f(BF16, 1, 32768, 64, 4, 32768) == 1 * 32768 * 4 * 192 * 2
+    assert f(BF16, 2, 300, 64, 8, 300) == 2 * 300 * 8 * 192 * 2
+    assert f(F32, 1, 512, 64, 8, 128) == 512 * 8 * 192 * 4
+    assert f(BF16, 1, 1000, 64, 8, 200) == 1000 * 8 * 192 * 2
+    assert f(BF16, 1, 1000, 12, 3, 128) == 1000 * 3 * 192 * 2      # 4 heads per KV head
+    assert f(BF16, 0, 10, 8, 8, 10) == 0 and f(BF16, 1, 10, 8, 3, 10) == 0  # invalid shapes

@@ -73,6 +73,36 @@ def test_prefill_rope(dtype, Hq, Hkv, L, W, layer):
     check_lse(lse, ref_lse, dtype)
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv,L,W,layer", [
+    ("bf16", 16, 2, 257, 10**9, "ga"),     # global kernel (64-key blocks, direct LDS staging)
+    ("bf16", 16, 4, 230, 64, "swa"),       # generic bf16 kernel (32-key blocks)
+    ("bf16", 64, 8, 300, 200, "swa"),      # a window past the ring kernel's
+    ("f32", 8, 1, 150, 10**9, "ga"),
+    ("f32", 64, 8, 200, 128, "swa"),
+])
+def test_prefill_rope_k_rotated_once(dtype, Hq, Hkv, L, W, layer):
+    # K rotated once into the workspace and K rotated at staging: the same arithmetic on the same
+    # values, so the same bits; both against the oracle
+    say(f"prefill rope, K rotated once vs at staging: {dtype} {Hq}/{Hkv} L={L} W={W}")
+    inp = prefill_inputs(43, 2, L, Hq, Hkv, 192, 128, W, dtype)
+    q, k, v = (gpu_from_numpy(x, dtype) for x in (inp.q, inp.k, inp.v))
+    s = torch.from_numpy(inp.sink).cuda()
+    table = mimo.rope_table(L, BASES[layer])
+    need = mimo.prefill_rope_workspace_size(q.dtype, 2, L, Hq, Hkv, W)
+    assert need == 2 * L * Hkv * 192 * (2 if dtype == "bf16" else 4)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")  # contents must not matter
+    o1, l1 = mimo.prefill(q, k, v, W, sink=s, scale=inp.scale, return_lse=True, rope=table, workspace=ws)
+    o2, l2 = mimo.prefill(q, k, v, W, sink=s, scale=inp.scale, return_lse=True, rope=table,
+                          rotate_k_once=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), (
+        float((o1.float() - o2.float()).abs().max()), float((l1 - l2).abs().max()))
+    ref_o, ref_lse = oracle.prefill_rope(f(inp.q, dtype), f(inp.k, dtype), f(inp.v, dtype), W, inp.sink,
+                                         inp.scale, BASES[layer])
+    assert_output_close(to_f64(o1), ref_o, dtype)
+    check_lse(to_f64(l1), ref_lse, dtype)
+
+
 def test_prefill_rope_changes_the_result():
     # guards against a path that ignores the table: unrotated attention differs from rotated
     inp = prefill_inputs(42, 1, 200, 16, 2, 192, 128, 128, "bf16")
