@@ -10,8 +10,9 @@ timed steps. One JSON line goes to stdout, with:
 
 * roofline - the dominant kernel's algorithmic bytes (or FLOPs) per launch divided by its average
   launch duration, timed with HIP events on the launch stream, against MI355X's published peak;
-* cpu_baseline - the float64 oracle timed on the host on a bounded leading slice of the same
-  workload (a reported baseline, not a target);
+* cpu_baseline - the float64 oracle timed on the host cores (a pool of forked worker processes,
+  one per core up to 16) over a bounded leading sample of the same workload, for the headline and
+  every other workload (a reported baseline, not a target);
 * secondary - the other measured workloads (fp32 prefill, global prefill, ring decode, split-KV
   global decode, both decodes at the 16K-context / 64-sequence MTP setting, the four bf16
   workloads with the rotary embedding fused, both decodes with 8-token block drafts, the commit
@@ -39,6 +40,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = os.path.join(ROOT, "sliding_window_sink_seeded_amd", "csrc")
 
 METRIC = "prefill attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
+
+# the other measured workloads, in the order they are timed
+SECONDARY = ("swa_prefill_f32", "ga_prefill_bf16", "swa_decode_bf16", "ga_decode_bf16",
+             "swa_decode_mtp_bf16", "ga_decode_mtp_bf16", "swa_prefill_rope_bf16",
+             "ga_prefill_rope_bf16", "swa_decode_rope_bf16", "ga_decode_rope_bf16",
+             "swa_decode_t8_bf16", "ga_decode_t8_bf16", "swa_backward_bf16", "ga_backward_bf16")
 
 
 def log(*a):
@@ -252,60 +259,157 @@ def _pad_q(rq, n_before):
     return q
 
 
-def cpu_baseline(case, target_s=12.0):
-    """Float64 oracle on the host over a leading slice of sequence 0 (exact for those rows)."""
+# ------------------------------------------------------------------ CPU baseline: the oracle
+
+# The workload, its inputs and the deadline of the CPU baseline being timed. Set before the worker
+# processes are forked (before anything touches the GPU), so the workers inherit it.
+_JOB = {}
+
+
+def cpu_workers():
+    """(worker processes, cores visible): the cores this process may run on, at most 16 workers
+    (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n)), n
+
+
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+
+    threadpool_limits(1)
+
+
+def _cpu_unit(unit):
+    """One unit of oracle work in a worker; returns (algorithmic FLOPs, algorithmic bytes) done,
+    (0, 0) when the unit starts past the deadline."""
     import numpy as np
 
     import oracle
     from sliding_window_sink_seeded_amd import workloads
     from sliding_window_sink_seeded_amd.inputs import as_float
 
-    w, inp, dt = case.w, case.inp, case.w.dtype
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    per_score = 2 * (3 * w.dqk + 2 * w.dv) if w.kind == "backward" else 2 * (w.dqk + w.dv)
-    if w.kind in ("prefill", "backward"):
-        def run(S):
-            q, k, v = (as_float(x[0:1, :S], dt) for x in (inp.q, inp.k, inp.v))
-            t0 = time.perf_counter()
-            if w.kind == "backward":
-                oracle.prefill_backward(q, k, v, as_float(case.d_o[0:1, :S], dt), w.window, inp.sink,
-                                        inp.scale)
-            else:
-                oracle.prefill(q, k, v, w.window, inp.sink, inp.scale)
-            return time.perf_counter() - t0, workloads.prefill_scores(1, S, w.Hq, min(w.window, S))
-
-        S = min(w.L, 512)
-        t, _ = run(S)
-        S2 = int(min(w.L, max(S, S * target_s / max(t, 1e-3))))
-        if w.window >= w.L:  # quadratic work in S
-            S2 = int(min(w.L, max(S, S * math.sqrt(target_s / max(t, 1e-3)))))
-        S2 = max(1, (S2 // 256) * 256) if S2 >= 256 else S2
-        t, scores = run(S2)
-        flops = scores * per_score
-        sample = f"sequence 0, query positions [0, {S2}) of {w.L}, all {w.Hq} heads"
+    if time.perf_counter() > _JOB["deadline"]:
+        return 0, 0
+    w, inp = _JOB["w"], _JOB["inp"]
+    f64 = lambda x: np.asarray(as_float(x, w.dtype), np.float64)
+    G = w.Hq // w.Hkv
+    if unit[0] == "rows":  # prefill rows [i0, i1) of sequence b, query heads of KV head g
+        _, b, i0, i1, g = unit
+        lo = max(0, i0 - w.window + 1)
+        q = f64(inp.q[b, i0:i1, g * G:(g + 1) * G])
+        k, v = f64(inp.k[b, lo:i1, g]), f64(inp.v[b, lo:i1, g])
+        if w.rope_base:
+            q = oracle.apply_rope(q, np.arange(i0, i1), w.rope_base)
+            k = oracle.apply_rope(k, np.arange(lo, i1), w.rope_base)
+        for j in range(G):
+            oracle.sink_attention(q[:, j], np.arange(i0, i1), k, np.arange(lo, i1), v,
+                                  float(inp.sink[g * G + j]), inp.scale, w.window)
+        scores = sum(min(i + 1, w.window) for i in range(i0, i1)) * G
+        return scores * 2 * (w.dqk + w.dv), 0
+    if unit[0] == "head":  # backward of one query head over the leading S rows of sequence 0
+        _, h, S = unit
+        g = h // G
+        sl = lambda x, j: f64(x[0:1, :S, j:j + 1])
+        oracle.prefill_backward(sl(inp.q, h), sl(inp.k, g), sl(inp.v, g), sl(_JOB["d_o"], h),
+                                w.window, inp.sink[h:h + 1], inp.scale)
+        return workloads.prefill_scores(1, S, 1, w.window) * 2 * (3 * w.dqk + 2 * w.dv), 0
+    _, b, g = unit  # decode: sequence b, KV head g with its G query heads
+    heads = np.arange(g * G, (g + 1) * G)
+    sel = lambda x, idx: f64(x[b:b + 1][:, :, idx])
+    args = (sel(inp.q, heads), sel(inp.k_new, [g]), sel(inp.v_new, [g]), sel(inp.k_cache, [g]),
+            sel(inp.v_cache, [g]), inp.cache_len[b:b + 1],
+            None if inp.cache_offset is None else inp.cache_offset[b:b + 1], w.window,
+            inp.sink[heads], inp.scale)
+    if w.rope_base:
+        oracle.decode_rope(*args, w.rope_base)
     else:
-        def run(nseq):
-            sel = list(range(nseq))
-            args = [as_float(x[sel], dt) for x in (inp.q, inp.k_new, inp.v_new, inp.k_cache, inp.v_cache)]
-            t0 = time.perf_counter()
-            oracle.decode(*args, inp.cache_len[sel],
-                          None if inp.cache_offset is None else inp.cache_offset[sel], w.window,
-                          inp.sink, inp.scale)
-            return time.perf_counter() - t0, workloads.decode_scores(inp.cache_len[sel], w.T, w.Hq, w.window)
+        oracle.decode(*args)
+    P = int(inp.cache_len[b])
+    flops = workloads.decode_scores(inp.cache_len[b:b + 1], w.T, G, w.window) * 2 * (w.dqk + w.dv)
+    nbytes = (w.T * G * (w.dqk + w.dv) + (min(P, w.window - 1) + w.T) * (w.dqk + w.dv)) * w.elem
+    return flops, nbytes
 
-        n = 1
-        t, _ = run(n)
-        n2 = int(min(w.B, max(1, n * target_s / max(t, 1e-3))))
-        t, scores = run(n2)
-        flops = scores * 2 * (w.dqk + w.dv)
-        sample = f"sequences [0, {n2}) of {w.B}, all {w.Hq} heads and {w.T} tokens"
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample, "seconds": round(t, 2)}
+
+def cpu_baseline(w, target_s):
+    """The float64 oracle as it stands, timed on the host over a bounded leading sample of workload
+    `w`, on a pool of forked worker processes (one BLAS thread each). Must run before the GPU is
+    initialised: the workers are forked from this process.
+
+    Units are dealt in order; those that would start after `target_s` are skipped, so the sample is
+    a leading part of the workload (prefill: rows of sequence 0 onwards; decode: (sequence, KV
+    head) pairs from sequence 0 on). The backward pass runs every query head over the leading S rows
+    of sequence 0, S sized by a one-head probe. The rate is in the workload's own unit: TFLOP/s of
+    visible scores for prefills and backward passes, GB/s of algorithmic bytes for decodes."""
+    import multiprocessing as mp
+
+    from sliding_window_sink_seeded_amd import inputs
+
+    workers, visible = cpu_workers()
+    dt = w.dtype
+    if w.kind in ("prefill", "backward"):
+        inp = inputs.prefill_inputs(w.seed, w.B, w.L, w.Hq, w.Hkv, w.dqk, w.dv, w.window, dt)
+        d_o = inputs.output_grad(w.seed, w.B, w.L, w.Hq, w.dv, dt) if w.kind == "backward" else None
+    else:
+        inp = inputs.decode_inputs(w.seed, w.B, w.T, w.Hq, w.Hkv, w.dqk, w.dv, w.C, w.window, dt,
+                                   cache_len=(w.P or None), len_range=(w.len_range or None),
+                                   ring_offsets=w.ring_offsets)
+        d_o = None
+    _JOB.clear()
+    _JOB.update(w=w, inp=inp, d_o=d_o, deadline=float("inf"))
+    if w.kind == "backward":
+        # one head over 256 rows in this process, then S so that all heads take about target_s
+        t0 = time.perf_counter()
+        _cpu_unit(("head", 0, 256))
+        t1 = max(time.perf_counter() - t0, 1e-3)
+        per_head = target_s * workers / w.Hq
+        grow = per_head / t1 if w.window < w.L else math.sqrt(per_head / t1)
+        S = int(min(w.L, max(256, (256 * grow) // 256 * 256)))
+        units = [("head", h, S) for h in range(w.Hq)]
+        sample = f"sequence 0, rows [0, {S}) of {w.L}, every one of {w.Hq} heads"
+    elif w.kind == "prefill":
+        units = [("rows", b, i0, min(w.L, i0 + 256), g) for b in range(w.B) for i0 in range(0, w.L, 256)
+                 for g in range(w.Hkv)]
+    else:
+        units = [("kv", b, g) for b in range(w.B) for g in range(w.Hkv)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_one_blas_thread) as pool:
+        pool.map(_noop, range(workers))  # worker start-up, untimed
+        # the workers hold copies of _JOB made at the fork: the deadline travels with each unit
+        deadline = time.perf_counter() + target_s if w.kind != "backward" else float("inf")
+        t0 = time.perf_counter()
+        done = pool.map(_cpu_timed_unit, [(u, deadline) for u in units], chunksize=1)
+        secs = time.perf_counter() - t0
+    flops = sum(f for f, _ in done)
+    nbytes = sum(b for _, b in done)
+    n_done = sum(1 for f, _ in done if f > 0)
+    if w.kind == "prefill":
+        sample = (f"the first {n_done} (block of 256 rows, KV head) units, sequence-major, of "
+                  f"{w.B} x {w.L} rows x {w.Hkv} KV heads (about {n_done * 256 // w.Hkv} rows, "
+                  f"all {w.Hq} query heads)")
+    elif w.kind == "decode":
+        sample = f"the first {n_done} of {w.B} x {w.Hkv} (sequence, KV head) pairs, all {w.T} tokens"
+    used = min(workers, len(units))
+    if w.kind == "decode":
+        value, unit = nbytes / secs / 1e9, "GB/s"
+    else:
+        value, unit = flops / secs / 1e12, "TFLOP/s"
+    _JOB.clear()
+    return {"value": value, "unit": unit, "cores": used, "kind": "oracle", "sample": sample,
+            "seconds": round(secs, 2), "workers": "processes (fork), 1 BLAS thread each",
+            "host_cores_visible": visible}
+
+
+def _noop(_):
+    return None
+
+
+def _cpu_timed_unit(arg):
+    unit, deadline = arg
+    _JOB["deadline"] = deadline
+    return _cpu_unit(unit)
 
 
 def kernel_source_digest(kind):
@@ -364,6 +468,10 @@ def main():
     ap.add_argument("--workload", default="swa_prefill_bf16")
     ap.add_argument("--no-secondary", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=2.0,
+                    help="wall-clock bound of the headline workload's CPU baseline")
+    ap.add_argument("--cpu-seconds-secondary", type=float, default=1.0,
+                    help="wall-clock bound of each other workload's CPU baseline")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--warm-seconds", type=float, default=0.25,
                     help="keep warming up (untimed) until this much time has passed")
@@ -376,9 +484,19 @@ def main():
               "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-
     from sliding_window_sink_seeded_amd import workloads
+
+    names = [args.workload] + ([] if args.no_secondary else [n for n in SECONDARY if n != args.workload])
+    cpu = {}
+    if not args.no_cpu_baseline:
+        # first, before anything touches the GPU: the oracle's worker processes fork from here
+        for name in names:
+            t0 = time.perf_counter()
+            cpu[name] = cpu_baseline(workloads.WORKLOADS[name],
+                                     args.cpu_seconds if name == args.workload else args.cpu_seconds_secondary)
+            log(f"[bench] {name}: cpu baseline {cpu[name]} ({time.perf_counter() - t0:.1f} s with inputs)")
+
+    import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -413,22 +531,16 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name, w.kind),
                 "algorithmic_per_launch": per_launch, "kernel_avg_ms": round(event_ms, 4)}
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(case)
     del case
     torch.cuda.empty_cache()
 
     secondary = []
     if not args.no_secondary:
-        for name in ("swa_prefill_f32", "ga_prefill_bf16", "swa_decode_bf16", "ga_decode_bf16",
-                     "swa_decode_mtp_bf16", "ga_decode_mtp_bf16", "swa_prefill_rope_bf16",
-                     "ga_prefill_rope_bf16", "swa_decode_rope_bf16", "ga_decode_rope_bf16",
-                     "swa_decode_t8_bf16", "ga_decode_t8_bf16", "swa_backward_bf16",
-                     "ga_backward_bf16"):
-            if name == w.name:
-                continue
+        for name in names[1:]:
             c = Case(workloads.WORKLOADS[name])
             sw, se = c.time(max(5, args.steps // 2), 3, args.warm_seconds)
             d = describe(c, sw, se)
+            d["cpu_baseline"] = cpu.get(name)
             log(f"[bench] {name}: {d}")
             secondary.append(d)
             del c
@@ -459,7 +571,7 @@ def main():
         "mfma_frac": head["mfma_frac"],
         "hbm_frac": head["hbm_frac"],
         "roofline": roofline,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu.get(w.name),
         "parity": parity,
         "secondary": secondary,
     }

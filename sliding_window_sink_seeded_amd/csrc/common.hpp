@@ -214,26 +214,64 @@ constexpr int kRopeDims = 64;
 // i0 + 32..; bf16 chunks carry 8 elements, fp32 chunks 4. Rotated values are rounded back to the
 // storage type (bf16: round to nearest even). The fused multiply-adds are written out so that every
 // kernel that inlines this rounds the same way (left to the compiler, contraction varied by kernel).
+// One rotated pair in fp32: x' = x c - y s, y' = y c + x s, with the multiply-adds written out.
+__device__ __forceinline__ float rope_x(float x, float y, float c, float s) { return __builtin_fmaf(x, c, -(y * s)); }
+__device__ __forceinline__ float rope_y(float x, float y, float c, float s) { return __builtin_fmaf(y, c, x * s); }
+
+// Two bf16 pairs packed as (x0, x1) in `lo` and (y0, y1) in `hi`, with (c0, s0, c1, s1).
+__device__ __forceinline__ void rope_bf16x2(uint32_t& lo, uint32_t& hi, float c0, float s0, float c1,
+                                            float s1) {
+  const float x0 = __uint_as_float(lo << 16), x1 = __uint_as_float(lo & 0xFFFF0000u);
+  const float y0 = __uint_as_float(hi << 16), y1 = __uint_as_float(hi & 0xFFFF0000u);
+  lo = pack_bf16x2(rope_x(x0, y0, c0, s0), rope_x(x1, y1, c1, s1));
+  hi = pack_bf16x2(rope_y(x0, y0, c0, s0), rope_y(x1, y1, c1, s1));
+}
+
 template <typename E>
 __device__ __forceinline__ void rope_rotate_chunk(u32x4& lo, u32x4& hi, const float* cs) {
   if constexpr (E::kBytes == 2) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float x0 = __uint_as_float(lo[w] << 16), x1 = __uint_as_float(lo[w] & 0xFFFF0000u);
-      const float y0 = __uint_as_float(hi[w] << 16), y1 = __uint_as_float(hi[w] & 0xFFFF0000u);
-      const float c0 = cs[4 * w], s0 = cs[4 * w + 1], c1 = cs[4 * w + 2], s1 = cs[4 * w + 3];
-      lo[w] = pack_bf16x2(__builtin_fmaf(x0, c0, -(y0 * s0)), __builtin_fmaf(x1, c1, -(y1 * s1)));
-      hi[w] = pack_bf16x2(__builtin_fmaf(y0, c0, x0 * s0), __builtin_fmaf(y1, c1, x1 * s1));
+      uint32_t x = lo[w], y = hi[w];
+      rope_bf16x2(x, y, cs[4 * w], cs[4 * w + 1], cs[4 * w + 2], cs[4 * w + 3]);
+      lo[w] = x;
+      hi[w] = y;
     }
   } else {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float x = __uint_as_float(lo[w]), y = __uint_as_float(hi[w]);
       const float c = cs[2 * w], s = cs[2 * w + 1];
-      lo[w] = __float_as_uint(__builtin_fmaf(x, c, -(y * s)));
-      hi[w] = __float_as_uint(__builtin_fmaf(y, c, x * s));
+      lo[w] = __float_as_uint(rope_x(x, y, c, s));
+      hi[w] = __float_as_uint(rope_y(x, y, c, s));
     }
   }
+}
+
+// Chunks of rotated dims per 32 dims (a pair's two elements sit in chunks j and j + kRopeH).
+template <typename E>
+inline constexpr int kRopeH = 32 / E::kPerChunk;
+
+// Rotation of a 16-byte chunk whose partner chunk sits in another lane of the same wave. `ch` is
+// the chunk's index within its head vector: chunks [0, H) hold dims 0..31, chunks [H, 2H) their
+// partners (dims + 32), H = kRopeH<E>; other chunks are returned unchanged. The caller lays the
+// chunks out so that the partner of chunk ch < H is at lane + H and that of chunk H <= ch < 2H at
+// lane - H. cs holds the (cos, sin) of pairs (ch % H) * kPerChunk .. + kPerChunk - 1 at the
+// vector's position (read only for rotated chunks). Every lane of the wave must call this: the
+// exchange reads the partner lane. Both lanes of a pair do the arithmetic of rope_rotate_chunk.
+template <typename E>
+__device__ __forceinline__ u32x4 rope_chunk_xlane(u32x4 x, int ch, int lane, const float* cs) {
+  constexpr int H = kRopeH<E>;
+  const int src = ch < H ? lane + H : (ch < 2 * H ? lane - H : lane);
+  u32x4 y;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) y[j] = (uint32_t)__shfl((int)x[j], src, 64);
+  if (ch < 2 * H) {
+    u32x4 lo = ch < H ? x : y, hi = ch < H ? y : x;
+    rope_rotate_chunk<E>(lo, hi, cs);
+    x = ch < H ? lo : hi;
+  }
+  return x;
 }
 
 // Loads n (cos, sin) pairs, n a multiple of 2, for dims i0 .. i0 + n - 1 at table row `pos`.
@@ -259,8 +297,8 @@ __device__ __forceinline__ void rope_rotate_frag(F& lo, F& hi, const float (&cs)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = lo[e], y = hi[e], c = cs[2 * e], s = cs[2 * e + 1];
-      lo[e] = __builtin_fmaf(x, c, -(y * s));
-      hi[e] = __builtin_fmaf(y, c, x * s);
+      lo[e] = rope_x(x, y, c, s);
+      hi[e] = rope_y(x, y, c, s);
     }
   }
 }

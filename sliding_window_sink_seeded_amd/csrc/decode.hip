@@ -118,7 +118,13 @@ struct KeyRows {
 // staged later by the caller). load() issues every global load of the thread, store() writes them
 // to LDS; a caller issues its first K/V block fetch in between. A non-default head map is read
 // before any other load, so that waiting for it waits for nothing else.
-template <typename E, int NCB>
+// ROPE (q and k_new arrive before the rotary embedding): load() also fetches the (cos, sin) of
+// every rotated chunk (query column c at position P + c % T, new token t at P + t) and store()
+// rotates the chunks in registers before writing them. A head vector's chunks go to consecutive
+// threads, and every vector starts at a thread index whose rotated chunks stay inside one wave
+// (vectors of 24 / 40 chunks for bf16, 48 / 80 for fp32), so a chunk's partner is 32 dims = H
+// lanes away in the same wave (rope_chunk_xlane).
+template <typename E, int NCB, bool ROPE>
 struct QStage {
   using Lds = DecodeLds<E, NCB>;
   static constexpr int kChunksRow = kDDQK / E::kPerChunk;
@@ -126,9 +132,20 @@ struct QStage {
   static constexpr int kQPer = (kQChunks + kDecNW * 64 - 1) / (kDecNW * 64);
   static constexpr int kKCh = kDDQK / E::kPerChunk, kVCh = kDDV / E::kPerChunk;
   static constexpr int kNewPer = (4 * (kKCh + kVCh) + kDecNW * 64 - 1) / (kDecNW * 64);
+  static constexpr int H = kRopeH<E>;
+  // A thread's Q chunks i = 0, 1, 2, .. sit at chunk (tid + 256 i) % kChunksRow of their rows; 256
+  // is 16 mod the row length (24 chunks bf16, 48 fp32) and 48 is 0 mod it, so the chunk indices
+  // repeat with period 3 and exactly one of every three, i = ir + 3 k, is a rotated chunk (< 2H).
+  static_assert((kDecNW * 64) % kChunksRow == 16 && (3 * 16) % kChunksRow == 0 && 3 * 2 * H == kChunksRow,
+                "one rotated chunk in every three");
+  static_assert(kQPer % 3 == 0, "whole periods");
+  static constexpr int kNR = ROPE ? kQPer / 3 : 1;  // rotated Q chunks per thread
+  static constexpr int kCs = ROPE ? 2 * E::kPerChunk : 1;
   u32x4 xq[kQPer], xn[kNewPer];
+  float qcs[kNR][kCs], ncs[ROPE ? kNewPer : 1][kCs];
+  int ir;  // ROPE: this thread's rotated Q chunks are i = ir + 3 k
 
-  __device__ __forceinline__ void load(const DecodeArgs& a, int tid, int b, int g, int cbase, int ncols) {
+  __device__ __forceinline__ void load(const DecodeArgs& a, int tid, int b, int g, int cbase, int ncols, int P) {
     const size_t krow_bytes = (size_t)kDDQK * E::kBytes, vrow_bytes = (size_t)kDDV * E::kBytes;
     int head[kQPer];
 #pragma unroll
@@ -146,6 +163,16 @@ struct QStage {
       const int c = cbase + min(u / kChunksRow, ncols - 1), ch = u % kChunksRow;
       xq[i] = ld16((const char*)a.q + (((size_t)b * a.T + c % a.T) * a.Hq + head[i]) * krow_bytes + ch * 16);
     }
+    if constexpr (ROPE) {
+      const int ch0 = tid % kChunksRow;
+      ir = ch0 < 2 * H ? 0 : (ch0 + 16 < kChunksRow + 2 * H && ch0 + 16 >= kChunksRow ? 1 : 2);
+#pragma unroll
+      for (int k = 0; k < kNR; ++k) {
+        const int u = tid + (ir + 3 * k) * kDecNW * 64;
+        const int c = cbase + min(u / kChunksRow, ncols - 1), ch = u % kChunksRow;
+        rope_load<E::kPerChunk>(a.rope, P + c % a.T, (ch % H) * E::kPerChunk, qcs[k]);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kNewPer; ++i) {
       const int u = tid + i * kDecNW * 64;
@@ -155,63 +182,52 @@ struct QStage {
                             : (const char*)a.v_new + (((size_t)b * a.T + t) * a.Hkv + g) * vrow_bytes +
                                   (ch - kKCh) * 16;
       xn[i] = ld16(src);
+      if constexpr (ROPE) {
+        if (ch < 2 * H) rope_load<E::kPerChunk>(a.rope, P + t, (ch % H) * E::kPerChunk, ncs[i]);
+      }
     }
   }
 
   // Q^T rows at smem, new tokens 0..3 (K rows, then V rows) right after them; the new tokens only
   // when `last` (the split that folds them in)
   __device__ __forceinline__ void store(char* smem, int tid, int ncols, bool last, int T) const {
+    const int lane = tid & 63;
+    u32x4 x[kQPer];
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) x[i] = xq[i];
+    if constexpr (ROPE) {
+      // the rotated chunk of each period of three; its partner lane rotates the same i
+#pragma unroll
+      for (int k = 0; k < kNR; ++k) {
+        const u32x4 v = ir == 0 ? x[3 * k] : (ir == 1 ? x[3 * k + 1] : x[3 * k + 2]);
+        const int ch = (tid + (ir + 3 * k) * kDecNW * 64) % kChunksRow;
+        const u32x4 r = rope_chunk_xlane<E>(v, ch, lane, qcs[k]);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) x[3 * k + j] = ir == j ? r : x[3 * k + j];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kQPer; ++i) {
       const int u = tid + i * kDecNW * 64;
       const int c = u / kChunksRow, ch = u % kChunksRow;
-      if (u < kQChunks) st16(smem + c * Lds::kQStride * E::kBytes + ch * 16, c < ncols ? xq[i] : zero_chunk());
+      if (u < kQChunks) st16(smem + c * Lds::kQStride * E::kBytes + ch * 16, c < ncols ? x[i] : zero_chunk());
     }
     char* snew = smem + Lds::kQBytes;
 #pragma unroll
     for (int i = 0; i < kNewPer; ++i) {
       const int u = tid + i * kDecNW * 64;
       const int t = u / (kKCh + kVCh), ch = u % (kKCh + kVCh);
+      u32x4 x = xn[i];
+      if constexpr (ROPE) x = rope_chunk_xlane<E>(x, ch < kKCh ? ch : 2 * H, lane, ncs[i]);  // V: as is
       if (last && u < 4 * (kKCh + kVCh) && t < T) {
         if (ch < kKCh)
-          st16(snew + t * kDDQK * E::kBytes + ch * 16, xn[i]);
+          st16(snew + t * kDDQK * E::kBytes + ch * 16, x);
         else
-          st16(snew + Lds::kNewKBytes + t * kDDV * E::kBytes + (ch - kKCh) * 16, xn[i]);
+          st16(snew + Lds::kNewKBytes + t * kDDV * E::kBytes + (ch - kKCh) * 16, x);
       }
     }
   }
 };
-
-// q and k_new arrive before the rotary embedding: rotate the staged Q^T rows and (last split) the
-// staged new-token K rows in LDS, query column c (token c % T) and new token t at positions
-// P + c % T and P + t; pairs (i, i + 32), i < 32. The caller synchronises before and after.
-template <typename E, int NCB>
-__device__ __forceinline__ void rope_staged(const DecodeArgs& a, char* smem, int tid, int P, int cbase,
-                                            int ncols, bool last) {
-  using Lds = DecodeLds<E, NCB>;
-  constexpr int kHalfRot = kRopeDims / 2;
-  const int n_q = ncols * kHalfRot, n_k = last ? a.T * kHalfRot : 0;
-  for (int u = tid; u < n_q + n_k; u += kDecNW * 64) {
-    const bool is_q = u < n_q;
-    const int uu = is_q ? u : u - n_q;
-    const int row = uu / kHalfRot, i = uu % kHalfRot;
-    const int pos = P + (is_q ? (cbase + row) % a.T : row);
-    char* base = is_q ? smem + row * Lds::kQStride * E::kBytes : smem + Lds::kQBytes + row * kDDQK * E::kBytes;
-    const f32x2 csn = *reinterpret_cast<const f32x2*>(a.rope + ((size_t)pos * kHalfRot + i) * 2);
-    if constexpr (E::kBytes == 2) {
-      uint16_t* e = reinterpret_cast<uint16_t*>(base);
-      const float x = __uint_as_float((uint32_t)e[i] << 16), y = __uint_as_float((uint32_t)e[i + kHalfRot] << 16);
-      e[i] = (uint16_t)bf16_bits(x * csn[0] - y * csn[1]);
-      e[i + kHalfRot] = (uint16_t)bf16_bits(y * csn[0] + x * csn[1]);
-    } else {
-      float* e = reinterpret_cast<float*>(base);
-      const float x = e[i], y = e[i + kHalfRot];
-      e[i] = x * csn[0] - y * csn[1];
-      e[i + kHalfRot] = y * csn[0] + x * csn[1];
-    }
-  }
-}
-
 
 // With one bf16 column block, asking for two waves per SIMD makes the compiler keep the
 // accumulators in VGPRs (169 registers, no AGPR copies) instead of 137 VGPRs + 80 AGPRs; both give
@@ -271,8 +287,8 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
   // latency overlaps them.
   char* sq = smem;
   {
-    QStage<E, NCB> st;
-    st.load(a, tid, b, g, cbase, ncols);
+    QStage<E, NCB, ROPE> st;
+    st.load(a, tid, b, g, cbase, ncols, P);
     if (key0 < s1) {
       const char *kr, *vr;
       rows(key0, kr, vr);
@@ -313,11 +329,6 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
   char* work = smem + Lds::kQBytes + Lds::kNewBytes;
   char* my_vt = work + wave * Lds::kVBytes;
   __syncthreads();  // Q^T and the new-token rows are in LDS
-
-  if constexpr (ROPE) {
-    rope_staged<E, NCB>(a, smem, tid, P, cbase, ncols, split == a.nsplit - 1);
-    __syncthreads();
-  }
 
   for (; key0 < s1; key0 += 32 * kDecNW) {
     cur.store_v(my_vt, col, half);
@@ -412,19 +423,32 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
 
   // ---- block drafts (T > 4, last split): new tokens 4 .. T-1 are staged only now, into the V
   // tiles of the work area (idle until the merge), when the registers of the key loop are free
-  // (staging them with the first four costs the whole kernel some 50 registers) ----
+  // (staging them with the first four costs the whole kernel some 50 registers). With ROPE their
+  // K rows are rotated on the way (positions P + 4 ..), laid out as in QStage: a row's chunks on
+  // consecutive threads, every row starting where its rotated chunks share one wave. ----
   char* snew_hi = work;  // K rows of tokens 4..7, then their V rows
   if (split == a.nsplit - 1 && a.T > 4) {
-    constexpr int kKCh = kDDQK / E::kPerChunk, kVCh = kDDV / E::kPerChunk;
+    constexpr int kKCh = kDDQK / E::kPerChunk, kVCh = kDDV / E::kPerChunk, kRow = kKCh + kVCh;
+    const int n = (a.T - 4) * kRow;
     __syncthreads();  // every wave is done with its V tile
-    for (int u = tid; u < (a.T - 4) * (kKCh + kVCh); u += kDecNW * 64) {
-      const int t = 4 + u / (kKCh + kVCh), ch = u % (kKCh + kVCh);
-      if (ch < kKCh)
-        st16(snew_hi + (t - 4) * kDDQK * E::kBytes + ch * 16,
-             ld16((const char*)a.k_new + (((size_t)b * a.T + t) * a.Hkv + g) * krow_bytes + ch * 16));
-      else
-        st16(snew_hi + Lds::kNewKBytes + (t - 4) * kDDV * E::kBytes + (ch - kKCh) * 16,
-             ld16((const char*)a.v_new + (((size_t)b * a.T + t) * a.Hkv + g) * vrow_bytes + (ch - kKCh) * 16));
+    for (int u0 = 0; u0 < n; u0 += kDecNW * 64) {  // same trip count in every lane (exchange below)
+      const int u = min(u0 + tid, n - 1);
+      const int t = 4 + u / kRow, ch = u % kRow;
+      u32x4 x = ch < kKCh
+                    ? ld16((const char*)a.k_new + (((size_t)b * a.T + t) * a.Hkv + g) * krow_bytes + ch * 16)
+                    : ld16((const char*)a.v_new + (((size_t)b * a.T + t) * a.Hkv + g) * vrow_bytes + (ch - kKCh) * 16);
+      if constexpr (ROPE) {
+        constexpr int H = kRopeH<E>;
+        float cs[2 * E::kPerChunk];
+        if (ch < 2 * H) rope_load<E::kPerChunk>(a.rope, P + t, (ch % H) * E::kPerChunk, cs);
+        x = rope_chunk_xlane<E>(x, ch < kKCh ? ch : 2 * H, lane, cs);
+      }
+      if (u0 + tid < n) {
+        if (ch < kKCh)
+          st16(snew_hi + (t - 4) * kDDQK * E::kBytes + ch * 16, x);
+        else
+          st16(snew_hi + Lds::kNewKBytes + (t - 4) * kDDV * E::kBytes + (ch - kKCh) * 16, x);
+      }
     }
     __syncthreads();
   }
@@ -635,6 +659,11 @@ void decode_window_kernel(const DecodeArgs a) {
   u32x4 vx = zero_chunk();
   const int tok_hi = wave + 4;
   const int nvx = EXT ? (a.T > 4 ? (a.T - 4) * (kDDV / E::kPerChunk) : 0) : 0;  // V chunks of tokens 4..T-1
+  // ROPE: (cos, sin) of all 32 pairs at that token's position; the rotated dims 0..63 are all in
+  // half 0's 96 elements, so a lane holds both chunks of each pair and rotates them itself (just
+  // before the token's score, when the loads have long landed)
+  constexpr int kXcs = (EXT && ROPE) ? kRopeDims : 1;
+  float xcs[kXcs];
   if constexpr (EXT) {
     const int t = min(tok_hi, a.T - 1);
     const char* krow = (const char*)a.k_new + (((size_t)b * a.T + t) * a.Hkv + g) * krow_bytes + half * (kDDQK / 2) * E::kBytes;
@@ -644,12 +673,15 @@ void decode_window_kernel(const DecodeArgs a) {
       const int tv = 4 + tid / (kDDV / E::kPerChunk), ch = tid % (kDDV / E::kPerChunk);
       vx = ld16((const char*)a.v_new + (((size_t)b * a.T + tv) * a.Hkv + g) * vrow_bytes + ch * 16);
     }
+    if constexpr (ROPE) {
+      if (half == 0) rope_load<kRopeDims / 2>(a.rope, P + t, 0, xcs);
+    }
   }
 
   KeyRows<E> cur;
   {
-    QStage<E, 1> st;
-    st.load(a, tid, b, g, cbase, ncols);
+    QStage<E, 1, ROPE> st;
+    st.load(a, tid, b, g, cbase, ncols, P);
     if (has_keys) {
       const int pos = min(key0 + col, s1 - 1);
       int slot = (pos + off) % a.C;
@@ -672,9 +704,11 @@ void decode_window_kernel(const DecodeArgs a) {
   float* xl = xs + 2 * kDecNW * 32;                                                  // [wave][col]
   static_assert(4 * kDecNW * 32 * 4 <= kDecNW * 64 * 4 * 2, "exchange area");
   __syncthreads();  // Q^T and the new-token rows are in LDS
-  if constexpr (ROPE) {
-    rope_staged<E, 1>(a, smem, tid, P, cbase, ncols, true);
-    __syncthreads();
+  if constexpr (EXT && ROPE) {
+    if (half == 0) {
+#pragma unroll
+      for (int j = 0; j < kRopeH<E>; ++j) rope_rotate_chunk<E>(kx[j], kx[j + kRopeH<E>], xcs + 2 * E::kPerChunk * j);
+    }
   }
 
   const bool cvalid = col < ncols;
@@ -908,10 +942,10 @@ size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit) {
 }
 
 // The one-pass window kernel serves a single split of at most four 32-key blocks with at most 32
-// query columns per workgroup and at most 4 new tokens (8 without RoPE).
+// query columns per workgroup and at most 8 new tokens.
 static bool window_kernel_fits(const DecodeArgs& a) {
   const bool cols = a.ncols <= 32 || a.chunk_cols == 32;  // every workgroup's chunk fits one column block
-  return a.nsplit == 1 && a.keys_per_split <= 32 * kDecNW && cols && (a.T <= kDecNW || (a.T <= 2 * kDecNW && !a.rope));
+  return a.nsplit == 1 && a.keys_per_split <= 32 * kDecNW && cols && a.T <= 2 * kDecNW;
 }
 
 // With one column block (e.g. 8 query heads x 4 tokens) a wave holds few blocks and fewer
@@ -925,7 +959,7 @@ static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t str
   const dim3 block(kDecNW * 64);
   if (bf16 && window_kernel_fits(a)) {
     if (a.T > kDecNW)
-      hipLaunchKernelGGL((decode_window_kernel<false, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_window_kernel<ROPE, true>), grid, block, 0, stream, a);
     else
       hipLaunchKernelGGL((decode_window_kernel<ROPE, false>), grid, block, 0, stream, a);
     return;

@@ -297,12 +297,11 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   auto rotate_block = [&](int sl, const float* trow) {
     const int r = tid / (kHalfRot / 2), i = 2 * (tid % (kHalfRot / 2));
     uint32_t* row = reinterpret_cast<uint32_t*>(smem + sl * Tile::kStageBytes + r * Tile::kKStride * 2);
-    const uint32_t lo = row[i / 2], hi = row[(i + kHalfRot) / 2];  // bf16 pairs (i, i+1), (i+32, i+33)
+    uint32_t lo = row[i / 2], hi = row[(i + kHalfRot) / 2];  // bf16 pairs (i, i+1), (i+32, i+33)
     const f32x4 c = *reinterpret_cast<const f32x4*>(trow + i * 2);
-    const float x0 = __uint_as_float(lo << 16), x1 = __uint_as_float(lo & 0xFFFF0000u);
-    const float y0 = __uint_as_float(hi << 16), y1 = __uint_as_float(hi & 0xFFFF0000u);
-    row[i / 2] = pack_bf16x2(x0 * c[0] - y0 * c[1], x1 * c[2] - y1 * c[3]);
-    row[(i + kHalfRot) / 2] = pack_bf16x2(y0 * c[0] + x0 * c[1], y1 * c[2] + x1 * c[3]);
+    rope_bf16x2(lo, hi, c[0], c[1], c[2], c[3]);  // the arithmetic of the rotation at staging
+    row[i / 2] = lo;
+    row[(i + kHalfRot) / 2] = hi;
   };
   static_assert(NT == kQT * kHalfRot / 2, "one thread per two pairs of a 32-row block");
   // this thread's 16 bytes of the (cos, sin) rows of positions p0 .. p0 + 31 (clamped into L)

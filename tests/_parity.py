@@ -15,6 +15,15 @@ TOL = {
     "bf16": dict(abs_max=2e-2, rel_l2=5e-3, lse_abs=2e-3),
 }
 
+# Gradients of the backward pass, at the same bars. Gradient magnitudes are not O(1) (dk sums over
+# every query of a window and every head of a group), so the bf16 max-error bar is taken relative
+# to the largest reference entry: max |err| <= 2e-2 max |ref|, relative L2 <= 5e-3. fp32: relative
+# max-norm and L2 errors <= 1e-5. Sink gradient: a sum of B * L terms exp(s_h - lse_i) D_i whose
+# sum can cancel, so its error is taken relative to the mass sum_i exp(s_h - lse_i) sum_d |dO o|;
+# bf16 rounds o before D is formed (relative 2^-9 per element) -> 4e-3, fp32 -> 1e-5.
+GRAD_TOL = {"f32": dict(rel_max=1e-5, rel_l2=1e-5), "bf16": dict(rel_max=2e-2, rel_l2=5e-3)}
+SINK_TOL = {"f32": 1e-5, "bf16": 4e-3}
+
 
 def say(*a):
     print(*a, flush=True)
@@ -45,6 +54,21 @@ def assert_output_close(got, ref, dtype, what="o"):
         ok = m["abs_max"] <= tol["abs_max"] and m["rel_l2"] <= tol["rel_l2"]
     assert ok, f"{what}: {m} exceeds {tol}"
     return m
+
+
+def assert_grad_close(got, ref, dtype, what):
+    m = metrics(got, ref)
+    tol = GRAD_TOL[dtype]
+    assert m["finite"], f"{what}: non-finite values"
+    assert m["rel_max"] <= tol["rel_max"] and m["rel_l2"] <= tol["rel_l2"], f"{what}: {m} vs {tol}"
+    return m
+
+
+def sink_grad_rel_err(dsink, ref_dsink, d_o, ref_o, ref_lse, sink):
+    """Per-head sink-gradient error relative to the mass of the terms it sums (see SINK_TOL)."""
+    Dabs = np.einsum("bihd,bihd->bhi", np.abs(d_o), np.abs(ref_o))
+    mass = (np.exp(np.asarray(sink, np.float64)[None, :, None] - ref_lse) * Dabs).sum(axis=(0, 2))
+    return np.abs(np.asarray(dsink, np.float64) - ref_dsink) / np.maximum(mass, 1e-30)
 
 
 def assert_lse_close(got, ref, dtype):

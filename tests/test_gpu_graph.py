@@ -19,7 +19,8 @@ import oracle
 import sliding_window_sink_seeded_amd as mimo
 from sliding_window_sink_seeded_amd.inputs import normal, output_grad, prefill_inputs
 
-from _parity import assert_lse_close, assert_output_close, f, gpu_from_numpy, say, to_f64
+from _parity import (SINK_TOL, assert_grad_close, assert_lse_close, assert_output_close, f, gpu_from_numpy,
+                     say, sink_grad_rel_err, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -153,15 +154,8 @@ def test_graph_prefill_and_backward(dtype, W, Hq, Hkv):
         assert_output_close(to_f64(o), ref_o, dtype)
         assert_lse_close(to_f64(lse), ref_lse, dtype)
         rq, rk, rv, rs = oracle.prefill_backward(*args, f(dO, dtype), W, inp.sink, inp.scale)
-        # the bars of the backward parity tests: relative to each gradient, and for the sink
-        # gradient relative to the mass of the terms it sums
-        tol = {"f32": (1e-4, 2e-5), "bf16": (2e-2, 1e-2)}[dtype]
+        # the method's gradient bars (tests/_parity.py GRAD_TOL, SINK_TOL)
         for name, got, ref in (("dq", grads[0], rq), ("dk", grads[1], rk), ("dv", grads[2], rv)):
-            d = to_f64(got) - ref
-            rel_max = np.abs(d).max() / np.abs(ref).max()
-            rel_l2 = np.linalg.norm(d) / np.linalg.norm(ref)
-            assert rel_max <= tol[0] and rel_l2 <= tol[1], (seed, name, rel_max, rel_l2)
-        Dabs = np.einsum("bihd,bihd->bhi", np.abs(f(dO, dtype)), np.abs(ref_o))
-        mass = (np.exp(inp.sink[None, :, None] - ref_lse) * Dabs).sum(axis=(0, 2))
-        err = np.abs(dsink_g.cpu().numpy().astype(np.float64) - rs) / np.maximum(mass, 1e-30)
-        assert err.max() <= {"f32": 1e-5, "bf16": 4e-3}[dtype], (seed, "dsink", err.max())
+            assert_grad_close(to_f64(got), ref, dtype, f"seed {seed} {name}")
+        err = sink_grad_rel_err(dsink_g.cpu().numpy(), rs, f(dO, dtype), ref_o, ref_lse, inp.sink)
+        assert err.max() <= SINK_TOL[dtype], (seed, "dsink", err.max())

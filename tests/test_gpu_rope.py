@@ -132,8 +132,9 @@ def run_decode_rope(inp, max_len, base, num_splits=0):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 4, 5, 8])
 def test_decode_rope_ring(dtype, T):
+    # T = 5..8: block drafts; new tokens 4..7 take their own staging path in both decode kernels
     say(f"decode rope ring {dtype} T={T}")
     lens = np.array([0, 1, 31, 127, 128, 300, 4097, 32767], np.int32)
     inp = decode_inputs(43 + T, len(lens), T, 64, 8, 192, 128, 128, 128, dtype, len_range=(0, 1))
@@ -158,9 +159,10 @@ def test_decode_rope_ring_column_chunks(B):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("num_splits", [1, 3])
-def test_decode_rope_global(dtype, num_splits):
-    say(f"decode rope global {dtype} splits={num_splits}")
-    inp = decode_inputs(47, 3, 4, 64, 4, 192, 128, 700, 10**9, dtype, len_range=(200, 700),
+@pytest.mark.parametrize("T", [4, 5, 8])
+def test_decode_rope_global(dtype, num_splits, T):
+    say(f"decode rope global {dtype} splits={num_splits} T={T}")
+    inp = decode_inputs(47 + T, 3, T, 64, 4, 192, 128, 700, 10**9, dtype, len_range=(200, 700),
                         ring_offsets=False)
     o, lse, ref_o, ref_lse = run_decode_rope(inp, 700, BASES["ga"], num_splits)
     assert_output_close(o, ref_o, dtype)
@@ -185,3 +187,24 @@ def test_decode_rope_continues_a_rope_prefill():
                            sink=G(inp.sink), scale=inp.scale, rope=table)
     torch.cuda.synchronize()
     assert_output_close(to_f64(o_dec), to_f64(o_pre[:, P:]), "f32")
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_ring_prefill_bits_do_not_depend_on_segments(rope):
+    # The sliding-window ring kernel cuts each sequence into segments of consecutive tiles whose
+    # length follows the grid (batch x KV heads). A tile at a segment start gets its window's key
+    # blocks from the segment prologue (with RoPE, rotated there in LDS); mid-segment they arrive one
+    # block per tile (rotated as they are staged). Alone, a 8192-token sequence runs in segments of
+    # 8 tiles; in a batch of 4, of 32 tiles. Its rows must come out bit for bit the same.
+    say(f"ring prefill segment invariance, rope={rope}")
+    L, Hq, Hkv, W = 8192, 64, 8, 128
+    inp = prefill_inputs(44, 4, L, Hq, Hkv, 192, 128, W, "bf16")
+    q, k, v = (gpu_from_numpy(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    s = torch.from_numpy(inp.sink).cuda()
+    table = mimo.rope_table(L, BASES["swa"]) if rope else None
+    o4, l4 = mimo.prefill(q, k, v, W, sink=s, scale=inp.scale, return_lse=True, rope=table)
+    o1, l1 = mimo.prefill(q[:1].contiguous(), k[:1].contiguous(), v[:1].contiguous(), W, sink=s,
+                          scale=inp.scale, return_lse=True, rope=table)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[0], o4[0]) and torch.equal(l1[0], l4[0]), (
+        float((o1[0].float() - o4[0].float()).abs().max()), float((l1[0] - l4[0]).abs().max()))
