@@ -17,8 +17,9 @@
  * Conventions shared by every entry point
  *  - Tensors are dense, row-major, last dimension contiguous, and 16-byte aligned.
  *  - Every pointer except `kv_head_of_q` is a DEVICE pointer owned by the caller. The library
- *    allocates nothing, frees nothing, keeps no state besides a thread-local error string, and
- *    never synchronises: work is enqueued on `stream` and the call returns.
+ *    allocates nothing, frees nothing and never synchronises: work is enqueued on `stream` and the
+ *    call returns. Its only state is a thread-local error string and, for
+ *    mimo_attn_decode_noalloc, a static device scratch array (and its address on each device).
  *  - All arguments are validated on the host before anything is launched. On a non-zero return
  *    nothing has been launched and no output has been written; mimo_attn_last_error() explains.
  *  - Device faults are asynchronous and surface at the caller's next synchronisation.
@@ -114,6 +115,29 @@ int mimo_attn_decode(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int
                      const float* sink, const int32_t* kv_head_of_q, float scale, int num_splits,
                      void* workspace, size_t workspace_bytes, void* o, float* lse,
                      hipStream_t stream);
+
+/*
+ * mimo_attn_decode for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, meaning and errors as
+ * mimo_attn_decode without the workspace: split-KV partial records go to a static device array of
+ * 64 MiB (67108864 bytes) inside the library, which every GPU the library runs on holds until the
+ * process ends. Nothing is allocated or freed by this call (its first call on a device looks up
+ * that device's address of the array once).
+ *  - Requests whose partials need more than 64 MiB (mimo_attn_decode_workspace_size() > 67108864)
+ *    return MIMO_EWORKSPACE; a smaller num_splits needs less.
+ *  - `stream` must belong to the current device (MIMO_EINVAL otherwise).
+ *  - Every call on one GPU shares that GPU's array and leaves its partials there: calls that
+ *    overlap in time on one GPU (other streams, other threads) race and give wrong results. Calls
+ *    ordered on one stream are safe. Nothing in the array needs to start at zero: every record a
+ *    call reads is written first by the same call.
+ */
+int mimo_attn_decode_noalloc(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
+                             const void* q, const void* k_new, const void* v_new,
+                             const void* k_cache, const void* v_cache, int C,
+                             const int32_t* cache_len, const int32_t* cache_offset,
+                             int max_cache_len, int window, const float* sink,
+                             const int32_t* kv_head_of_q, float scale, int num_splits, void* o,
+                             float* lse, hipStream_t stream);
 
 /*
  * Rotary position embedding of the leading Q/K dimensions (MiMo-V2-Flash Technical Report review

@@ -26,7 +26,7 @@ __all__ = ["prefill", "decode", "decode_workspace_size", "prefill_rope_workspace
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmimo_attn.so")
 EXPORTS = ("mimo_attn_prefill", "mimo_attn_decode", "mimo_attn_decode_workspace_size",
            "mimo_attn_rope_table", "mimo_attn_prefill_rope", "mimo_attn_prefill_rope_workspace_size",
-           "mimo_attn_decode_rope",
+           "mimo_attn_decode_rope", "mimo_attn_decode_noalloc",
            "mimo_attn_prefill_backward", "mimo_attn_prefill_backward_workspace_size",
            "mimo_attn_cache_append",
            "mimo_attn_last_error", "mimo_attn_version")
@@ -73,6 +73,9 @@ def library() -> ctypes.CDLL:
                                           i32, vp, vp, i32, i32, vp, vp, f32, vp, i32, i32, i32, vp,
                                           sz, vp, vp, vp]
     lib.mimo_attn_decode_rope.restype = i32
+    lib.mimo_attn_decode_noalloc.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                             i32, vp, vp, i32, i32, vp, vp, f32, i32, vp, vp, vp]
+    lib.mimo_attn_decode_noalloc.restype = i32
     lib.mimo_attn_prefill_backward.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                                 vp, vp, i32, vp, vp, f32, vp, vp, vp, vp, vp, sz,
                                                 vp]
@@ -252,8 +255,10 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_len, window: int, max_cache_
 
     q [B, T, Hq, dqk]; k_new/v_new [B, T, Hkv, d]; k_cache/v_cache [B, C, Hkv, d];
     cache_len / cache_offset int32 [B] GPU tensors. rope: None, or a table from rope_table() when
-    q and k_new are given before the rotary embedding (the cache holds rotated keys). Returns
-    (o, lse or None).
+    q and k_new are given before the rotary embedding (the cache holds rotated keys). workspace:
+    None (allocated here when the split plan needs one), a uint8 tensor, or "static" for
+    mimo_attn_decode_noalloc (the library's static scratch; with out, and lse if wanted, given,
+    the call allocates nothing). Returns (o, lse or None).
     """
     import torch
 
@@ -280,11 +285,23 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_len, window: int, max_cache_
         _dev(lse, "lse", torch.float32, 3)
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
+    keep, kvm = _kv_map(kv_map, Hq)
+    if workspace == "static":  # the library's static scratch: nothing is allocated
+        if rope is not None:
+            raise ValueError("the static-scratch decode takes rotated q / k_new (rope=None)")
+        rc = library().mimo_attn_decode_noalloc(dt, B, T, Hq, Hkv, dqk, dv, _ptr(q), _ptr(k_new),
+                                                _ptr(v_new), _ptr(k_cache), _ptr(v_cache), C,
+                                                _ptr(cache_len), _ptr(cache_offset),
+                                                int(max_cache_len), int(window), _ptr(sink), kvm,
+                                                float(scale), int(num_splits), _ptr(out), _ptr(lse),
+                                                _stream(stream))
+        del keep
+        _check(rc)
+        return out, lse
     ws_bytes = decode_workspace_size(B, T, Hq, Hkv, dv, max_cache_len, window, num_splits)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    keep, kvm = _kv_map(kv_map, Hq)
     if rope is None:
         rc = library().mimo_attn_decode(dt, B, T, Hq, Hkv, dqk, dv, _ptr(q), _ptr(k_new), _ptr(v_new),
                                         _ptr(k_cache), _ptr(v_cache), C, _ptr(cache_len),

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/mimo_attn.h"
@@ -306,15 +307,60 @@ size_t mimo_attn_decode_workspace_size(int B, int T, int Hq, int Hkv, int d_v, i
 
 }  // extern "C"
 
+// ------------------------------------------------------------------------ decode without allocation
+//
+// mimo_attn_decode for callers that cannot allocate device memory (code under HIP graph capture,
+// serving loops, harnesses that forbid hipMalloc): the split-KV partial records go to `scratch`, a
+// static device array of kNoallocScratchBytes that every GPU the library runs on holds until the
+// process ends. Host code never uses the array's name as a device address: its address on each
+// device comes from hipGetSymbolAddress, taken once per device (with that device current) on the
+// first call there that needs partials, and kept in g_scratch_dev.
+
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+
+// This device's address of `scratch` for launches on `stream` (which must belong to the current
+// device, the one the address is taken on).
+int scratch_address(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(MIMO_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  hipDevice_t sdev = 0;
+  e = hipStreamGetDevice(stream, &sdev);
+  if (e != hipSuccess) return fail(MIMO_EHIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+  if ((int)sdev != cur)
+    return fail(MIMO_EINVAL, "the stream belongs to device %d but device %d is current", (int)sdev, cur);
+  if (cur < 0 || cur >= kMaxDevices) return fail(MIMO_EUNSUPPORTED, "device %d beyond %d", cur, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[cur]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MIMO_EHIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_dev[cur] = p;
+  }
+  *out = g_scratch_dev[cur];
+  return MIMO_OK;
+}
+
+}  // namespace
+
 namespace {
 
 // rope: NULL, or a table of at least max_cache_len + T positions for unrotated q / k_new
+// static_ws: the partials go to the library's static scratch (workspace arguments unused)
 int decode_impl(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v, const void* q,
                 const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
                 int C, const int32_t* cache_len, const int32_t* cache_offset, int max_cache_len,
                 int window, const float* sink, const int32_t* kv_head_of_q, float scale,
                 const float* rope, int num_splits, void* workspace, size_t workspace_bytes,
-                void* o, float* lse, hipStream_t stream) {
+                void* o, float* lse, hipStream_t stream, bool static_ws = false) {
   if (int rc = check_common(dt, B, Hq, Hkv, d_qk, d_v, window, scale)) return rc;
   if (T < 1 || T > mimo::kMaxNew) return fail(MIMO_EINVAL, "T must be in 1..%d (got %d)", mimo::kMaxNew, T);
   if (max_cache_len < 0 || max_cache_len > (1 << 30) - 8)
@@ -337,6 +383,14 @@ int decode_impl(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
   if ((double)B * C * Hkv * d_qk * elem > 4.6e18) return fail(MIMO_EINVAL, "cache too large");
 
   const DecodePlan plan = plan_decode(B, T, Hq, Hkv, max_cache_len, window, num_splits);
+  if (static_ws && plan.ws_bytes > 0) {
+    if (plan.ws_bytes > kNoallocScratchBytes)
+      return fail(MIMO_EWORKSPACE,
+                  "the split partials need %zu bytes, the library's static decode scratch holds %zu "
+                  "(a smaller num_splits needs less)", plan.ws_bytes, kNoallocScratchBytes);
+    if (int rc = scratch_address(stream, &workspace)) return rc;
+    workspace_bytes = kNoallocScratchBytes;
+  }
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes)
       return fail(MIMO_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
@@ -399,6 +453,23 @@ int mimo_attn_decode_rope(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk
   return decode_impl(dt, B, T, Hq, Hkv, d_qk, d_v, q, k_new, v_new, k_cache, v_cache, C, cache_len,
                      cache_offset, max_cache_len, window, sink, kv_head_of_q, scale, rope_table,
                      num_splits, workspace, workspace_bytes, o, lse, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int mimo_attn_decode_noalloc(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
+                             const void* q, const void* k_new, const void* v_new,
+                             const void* k_cache, const void* v_cache, int C,
+                             const int32_t* cache_len, const int32_t* cache_offset,
+                             int max_cache_len, int window, const float* sink,
+                             const int32_t* kv_head_of_q, float scale, int num_splits, void* o,
+                             float* lse, hipStream_t stream) {
+  g_err.clear();
+  return decode_impl(dt, B, T, Hq, Hkv, d_qk, d_v, q, k_new, v_new, k_cache, v_cache, C, cache_len,
+                     cache_offset, max_cache_len, window, sink, kv_head_of_q, scale, nullptr,
+                     num_splits, nullptr, 0, o, lse, stream, true);
 }
 
 }  // extern "C"

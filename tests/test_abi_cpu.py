@@ -125,6 +125,31 @@ def test_decode_validation(lib, kw, code):
     assert mimo.last_error() != ""
 
 
+def decode_noalloc(lib, dt=BF16, B=4, T=4, Hq=64, Hkv=8, dqk=192, dv=128, q=P, kn=P, vn=P, kc=P, vc=P,
+                   C=128, lens=P, offs=None, max_len=1000, window=128, sink=None, kvm=None, scale=0.07,
+                   nsplit=0, o=P, lse=None):
+    return lib.mimo_attn_decode_noalloc(dt, B, T, Hq, Hkv, dqk, dv, q, kn, vn, kc, vc, C, lens, offs,
+                                        max_len, window, sink, kvm, scale, nsplit, o, lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=9), EINVAL),
+    (dict(C=126), EINVAL),
+    (dict(lens=None), EINVAL),
+    (dict(dqk=64), EUNSUPPORTED),
+    (dict(scale=0.0), EINVAL),
+    # partials beyond the 64 MiB static scratch: 64 x 4 KV heads x 64 splits x 128 columns x 132
+    # floats = 1.1 GB
+    (dict(B=64, T=8, Hkv=4, window=10**9, C=262144, max_len=262144, nsplit=64), EWORKSPACE),
+])
+def test_decode_noalloc_validation(lib, kw, code):
+    # the same checks as mimo_attn_decode, all before anything reaches HIP
+    assert decode_noalloc(lib, **kw) == code
+    assert mimo.last_error() != ""
+    if code == EWORKSPACE:
+        assert "static decode scratch" in mimo.last_error()
+
+
 def test_small_ring_is_enough_when_history_is_short(lib):
     # C >= min(W - 1, max_len): with max_len = 100 a 100-slot ring holds every committed key; the
     # call then fails only on the workspace (forced split) - validation of C passed.
