@@ -238,6 +238,295 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
     a.lse[((size_t)b * a.Hq + head) * a.L + qpos] = (m + fast_log2(l)) * kLn2;
 }
 
+// ------------------------------------------------------------ global (causal) ping-pong kernel
+
+#ifndef MIMO_GA_PINGPONG
+#define MIMO_GA_PINGPONG 1
+#endif
+#ifndef MIMO_GA_DEPTH
+#define MIMO_GA_DEPTH 4
+#endif
+#ifndef MIMO_GA_SGB
+#define MIMO_GA_SGB 1
+#endif
+#ifndef MIMO_GA_PRIO
+#define MIMO_GA_PRIO 0
+#endif
+//
+// bf16 global attention with 8 query heads per workgroup (wave w = head w of the chunk, all on the
+// same 32 query rows; waves w and w + 4 share a SIMD). Each wave alternates MFMA phases
+// M_k = [O^T += V^T P^T of block k - 1, S^T = K Q^T of block k] and softmax phases V_k (masking,
+// running max, exponentials, P to bf16 fragments, rescale). Waves 0-3 (group A) run one phase
+// ahead of waves 4-7 (group B), so on every SIMD one wave issues MFMAs while the other works on
+// the VALU; a barrier closes every phase ("slot"):
+//     slot 2k:   A runs M_k,  B runs V_{k-1}          slot 2k + 1:  A runs V_k,  B runs M_k
+// With n blocks there are 2n + 2 slots, and every wave passes the same 2n + 3 barriers (one after
+// the prologue). Block b is read in slots 2b .. 2b + 3, so three LDS stages rotate: block b + 1 is
+// loaded into registers at the start of slot 2b and stored, into the stage block b - 2 held, at
+// the end of slot 2b + 1, two slots of latency later.
+// Scheduling-group pattern of an M phase (masks: 0x100 LDS reads, 0x008 MFMA): the reads of the
+// first D operand fragments, then product i followed by the reads of fragment i + D. Fragments of
+// the first NPV products (V^T) take two transposing reads, the others (K) one.
+template <int NPV, int NM, int D, int I>
+struct GaReadAhead {
+  static constexpr int reads(int i) { return i < NPV ? 2 : 1; }
+  static constexpr int first() {
+    int r = 0;
+    for (int i = 0; i < D && i < NM; ++i) r += reads(i);
+    return r;
+  }
+  __device__ __forceinline__ static void emit() {
+    if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, first(), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I + D < NM) __builtin_amdgcn_sched_group_barrier(0x100, reads(I + D), 0);
+    if constexpr (I + 1 < NM) GaReadAhead<NPV, NM, D, I + 1>::emit();
+  }
+};
+
+template <int ROPE>
+__global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a) {
+  using E = BF16;
+  using Tile = PrefillTile<E, 64>;
+  using Frag = bf16x8;
+  constexpr int NW = 8, BK = 64, NS = 3;
+  __shared__ __attribute__((aligned(16))) char smem[NS * Tile::kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: one phase ahead, 1: one phase behind
+
+  // heaviest query blocks (latest positions) first; consecutive workgroups differ in (KV head,
+  // head chunk)
+  const int per_q = a.B * a.Hkv * a.n_hchunks;
+  const int qb = a.n_qblocks - 1 - (int)(blockIdx.x / per_q);
+  int rest = blockIdx.x % per_q;
+  const int hc = rest % a.n_hchunks;
+  rest /= a.n_hchunks;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  const int head = a.hl.at(g * a.G + hc * NW + wave);
+  const int p0 = qb * kQT;  // the workgroup's (and every wave's) first query row
+  const int qpos = p0 + col;
+  const int P1 = min(a.L, p0 + kQT);
+  const int n = (P1 + BK - 1) / BK;  // key blocks [0, P1)
+
+  const size_t krow_stride = (size_t)a.Hkv * kDQK * 2;
+  const size_t vrow_stride = (size_t)a.Hkv * kDV * 2;
+  const char* kbase = (const char*)a.k + ((size_t)b * a.L * a.Hkv + g) * kDQK * 2;
+  const char* vbase = (const char*)a.v + ((size_t)b * a.L * a.Hkv + g) * kDV * 2;
+
+  // K/V blocks are staged through registers (global loads, later LDS stores), not loaded straight
+  // into LDS: the compiler makes every LDS read of a wave wait for all of its loads that target LDS
+  // (it cannot tell the stages apart), which would stall the next MFMA phase on the prefetch.
+  KVStager<E, 512, BK> st;
+  st.init(krow_stride, vrow_stride, tid);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    if (j < n) {
+      st.load(kbase, vbase, krow_stride, vrow_stride, j * BK, a.L, tid);
+      st.store(smem + j * Tile::kStageBytes, tid);
+    }
+  }
+  Frag qf[kDQK / 16];
+  {
+    const int qload = min(qpos, a.L - 1);
+    const char* qrow = (const char*)a.q + (((size_t)b * a.L + qload) * a.Hq + head) * kDQK * 2;
+#pragma unroll
+    for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
+    if constexpr (ROPE != kPreRopeNone) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float cs[16];
+        rope_load<8>(a.rope, qload, 16 * kk + 8 * half, cs);
+        rope_rotate_frag<E>(qf[kk], qf[kk + 2], cs);
+      }
+    }
+  }
+
+  const float c = a.scale_log2;
+  const float sink_l2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
+  float m = sink_l2;
+  float l = a.sink ? 1.f : 0.f;
+  f32x16 acc[kDV / 32];
+#pragma unroll
+  for (int db = 0; db < kDV / 32; ++db) acc[db] = zero16();
+  f32x16 s[2];
+  Frag pf[BK / 16];
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) pf[ks] = Frag{};
+
+  wait_vm();
+  __syncthreads();
+
+  // LDS addresses: the stages' base, and this lane's offsets within a stage for the V^T fragments
+  // (transposing reads: row 4 half + (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4))
+  // and the K fragments (row col, column 8 half)
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  const uint32_t vt_lane = ((4 * half + ((lane & 15) >> 2)) * Tile::kVStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  const uint32_t k_lane = (col * Tile::kKStride + 8 * half) * 2;
+
+  // M_k: the previous block's PV products (PV), then this block's scores (QK). With one wave per
+  // SIMD issuing MFMAs at a time, nothing else hides the LDS latency of their operands: every
+  // operand fragment is read D products ahead of its use.
+  auto mphase = [&](int k, auto pv_tag, auto qk_tag) {
+    constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
+#if MIMO_GA_PRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
+    constexpr int NPV = PV ? 16 : 0, NM = NPV + (QK ? 24 : 0), D = MIMO_GA_DEPTH;
+    // this lane's addresses in the stages of blocks k - 1 (V) and k (K); every fragment is then at
+    // a constant offset from them (the LDS read's offset field). The empty asm keeps the compiler
+    // from re-associating them into one hoisted register per fragment.
+    uint32_t vb = lds_base + ((k + NS - 1) % NS) * Tile::kStageBytes + Tile::kKBytes + vt_lane;
+    uint32_t kb = lds_base + (k % NS) * Tile::kStageBytes + k_lane;
+    asm volatile("" : "+v"(vb), "+v"(kb));
+    auto frag = [&](int i) -> Frag {  // A operand of product i
+      if (i < NPV) {
+        const int ks = i / 4, db = i % 4;
+        const uint32_t a0 = vb + (16 * ks * Tile::kVStride + 32 * db) * 2;
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)a0);
+        const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(uintptr_t)(a0 + 8 * Tile::kVStride * 2));
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        s16x8 u;
+        u[0] = x[0]; u[1] = x[1]; u[2] = x[2]; u[3] = x[3];
+        u[4] = y[0]; u[5] = y[1]; u[6] = y[2]; u[7] = y[3];
+        return __builtin_bit_cast(bf16x8, u);
+      }
+      const int j = i - NPV;
+      const uint32_t a0 = kb + (32 * (j % 2) * Tile::kKStride + 16 * (j / 2)) * 2;
+      return __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)a0);
+    };
+    Frag buf[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (i < NM) buf[i] = frag(i);
+    if constexpr (QK) {
+      s[0] = zero16();
+      s[1] = zero16();
+    }
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const Frag x = buf[i % D];
+      if (i + D < NM) buf[i % D] = frag(i + D);
+      if (i < NPV) {
+        acc[i % 4] = mma(x, pf[i / 4], acc[i % 4]);
+      } else {
+        const int j = i - NPV;
+        s[j % 2] = mma(x, qf[j / 2], s[j % 2]);
+      }
+    }
+#if MIMO_GA_SGB
+    // keep that order: the first D fragments' reads, then one product and the next reads, ...
+    GaReadAhead<NPV, NM, D, 0>::emit();
+#endif
+#if MIMO_GA_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
+  };
+
+  // V_k: softmax of block k (masked only for the last block, which holds the diagonal)
+  auto vphase = [&](int k, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (MASKED) {
+          const int key = k * BK + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
+          s[sb][r] = key <= qpos ? s[sb][r] : -INFINITY;
+        }
+        bmax = fmaxf(bmax, s[sb][r]);
+      }
+    }
+    const float mb = halves_max(bmax) * c;
+    if (__builtin_amdgcn_ballot_w64(mb > m + kLazyRescale || (m == -INFINITY && mb > m)) != 0) {
+      const float m_new = fmaxf(m, mb);
+      const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.f : m_new));
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDV / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      m = m_new;
+    }
+    const float m_use = (m == -INFINITY) ? 0.f : m;
+    float rs = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[sb][r], c, -m_use));
+        s[sb][r] = p;
+        rs += p;
+      }
+    }
+    l += halves_sum(rs);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) pf[ks] = frag_from_acc<E>(s[ks >> 1], 8 * (ks & 1));
+  };
+
+  // barrier that closes a slot
+  auto close_slot = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // block kb + 1 is loaded into registers at the start of slot 2 kb and stored into the stage of
+  // block kb - 2 (read last in slot 2 kb - 1) at the end of slot 2 kb + 1, by every wave
+  auto load_at = [&](int kb) {
+    if (kb >= 2 && kb + 1 < n) st.load(kbase, vbase, krow_stride, vrow_stride, (kb + 1) * BK, a.L, tid);
+  };
+  auto store_at = [&](int kb) {
+    if (kb >= 2 && kb + 1 < n) st.store(smem + ((kb + 1) % NS) * Tile::kStageBytes, tid);
+  };
+  const std::false_type no{};
+  const std::true_type yes{};
+  if (grp == 0) {
+    mphase(0, no, yes);
+    close_slot();                          // slot 0
+    for (int k = 0; k + 1 < n; ++k) {
+      vphase(k, no);
+      store_at(k);
+      close_slot();                        // slot 2k + 1
+      load_at(k + 1);
+      mphase(k + 1, yes, yes);
+      close_slot();                        // slot 2k + 2
+    }
+    vphase(n - 1, yes);
+    store_at(n - 1);
+    close_slot();                          // slot 2n - 1
+    mphase(n, yes, no);
+    close_slot();                          // slot 2n
+    close_slot();                          // slot 2n + 1 (idle)
+  } else {
+    close_slot();                          // slot 0 (idle)
+    mphase(0, no, yes);
+    close_slot();                          // slot 1
+    for (int k = 0; k + 1 < n; ++k) {
+      load_at(k + 1);
+      vphase(k, no);
+      close_slot();                        // slot 2k + 2
+      mphase(k + 1, yes, yes);
+      store_at(k + 1);
+      close_slot();                        // slot 2k + 3
+    }
+    vphase(n - 1, yes);
+    close_slot();                          // slot 2n
+    mphase(n, yes, no);
+    close_slot();                          // slot 2n + 1
+  }
+
+  const bool valid = qpos < a.L;
+  char* orow = (char*)a.o + (((size_t)b * a.L + min(qpos, a.L - 1)) * a.Hq + head) * kDV * 2;
+  store_out_row<E>(orow, acc, 1.f / l, half, valid);
+  if (a.lse && half == 0 && valid) a.lse[((size_t)b * a.Hq + head) * a.L + qpos] = (m + fast_log2(l)) * kLn2;
+}
+
 // ---------------------------------------------------------------- sliding-window ring kernel
 
 template <int NB, bool ROPE>
@@ -517,6 +806,24 @@ static hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+
+// bf16 global attention, 8 query heads per workgroup: the ping-pong kernel (with RoPE only when K
+// is rotated once into k_ws beforehand)
+static hipError_t launch_global(const PrefillArgs& a, hipStream_t stream) {
+  const long long n_wg = (long long)a.n_qblocks * a.B * a.Hkv * a.n_hchunks;
+  if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (a.rope) {
+    const long long units = (long long)a.B * a.L * a.Hkv * (kDQK / 8);
+    hipLaunchKernelGGL(rope_k_kernel<BF16>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, a);
+    PrefillArgs r = a;
+    r.k = a.k_ws;
+    hipLaunchKernelGGL(prefill_global_kernel<kPreRopeQ>, dim3((unsigned)n_wg), dim3(512), 0, stream, r);
+  } else {
+    hipLaunchKernelGGL(prefill_global_kernel<kPreRopeNone>, dim3((unsigned)n_wg), dim3(512), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
 // Segment sizing of the ring kernel: about this many workgroups per compute unit over the grid
 // (one: a single generation of long segments; 1, 2, 4, 8, 16 per CU measured 1.276, 1.284, 1.289,
 // 1.315, 1.357 ms on the 4 x 32768 workload),
@@ -599,6 +906,7 @@ hipError_t prefill_launch(bool bf16, PrefillArgs a, hipStream_t stream) {
       default: return launch_swa<5>(a, stream);
     }
   }
+  if (global && MIMO_GA_PINGPONG && hg == NW && (!a.rope || a.k_ws)) return launch_global(a, stream);
   if (global) return launch<BF16, NW, 64>(a, stream);
   return launch<BF16, NW, 32>(a, stream);
 }

@@ -218,7 +218,8 @@ struct KVStagerDMA {
     }
   }
 
-  // Issues this wave's loads of the block starting at key0 into `stage`.
+  // Issues this wave's loads of the block starting at key0 into `stage`. Only a block that reaches
+  // past L needs the lane's row again (integer divisions): a uniform branch around it.
   __device__ __forceinline__ void load(char* stage, const char* kbase, const char* vbase, size_t kstride,
                                        size_t vstride, int key0, int L, int wave, int lane) const {
     const bool tail = key0 + BK > L;
@@ -228,11 +229,14 @@ struct KVStagerDMA {
       if (u >= kInst) break;  // uniform per wave
       const bool is_k = u < kKInst;
       const char* p = (is_k ? kbase + (size_t)key0 * kstride : vbase + (size_t)key0 * vstride) + off[i];
-      int row, ch;
-      const bool active = row_chunk(u, lane, row, ch);
-      if (tail) p += ((size_t)min(key0 + row, L - 1) - (key0 + row)) * (is_k ? kstride : vstride);
+      if (tail) {
+        int row, ch;
+        row_chunk(u, lane, row, ch);
+        p += ((size_t)min(key0 + row, L - 1) - (key0 + row)) * (is_k ? kstride : vstride);
+      }
       char* dst = stage + (is_k ? 1024 * u : Tile::kKBytes + 1024 * (u - kKInst));
       const bool partial = is_k ? (u == kKInst - 1 && kKChunks % 64) : (u == kInst - 1 && kVChunks % 64);
+      const bool active = 64 * (is_k ? u : u - kKInst) + lane < (is_k ? kKChunks : kVChunks);
       if (!partial || active)
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)p,
                                          (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
