@@ -14,6 +14,10 @@ namespace {
 
 // Query columns per workgroup of a single-pass decode with more than 32 columns (see decode_impl).
 constexpr int kChunkCols1Split = 32;
+#ifndef MIMO_WIN_COLS
+#define MIMO_WIN_COLS 64
+#endif
+constexpr int kWindowCols = MIMO_WIN_COLS;
 
 
 thread_local std::string g_err;
@@ -415,6 +419,10 @@ int decode_impl(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
   // reading the short K/V history once with the 64-column kernel (8 heads x 8 tokens: 107 vs
   // 147 us).
   a.chunk_cols = (plan.nsplit == 1 && a.ncols > 32) ? kChunkCols1Split : mimo::kMaxCols;
+  // bf16 single passes over at most four 32-key blocks run the one-pass window kernel, which
+  // takes two column blocks per workgroup (each K / V fragment then feeds two products)
+  if (dt == MIMO_BF16 && plan.nsplit == 1 && plan.keys_per_split <= 128 && a.ncols > 32)
+    a.chunk_cols = kWindowCols;
   a.n_chunks = (a.ncols + a.chunk_cols - 1) / a.chunk_cols;
   if ((long long)a.Hkv * a.n_chunks > 65535) return fail(MIMO_EUNSUPPORTED, "too many KV heads x column chunks");
   if (int rc = group_heads(Hq, Hkv, kv_head_of_q, &a.hl)) return rc;

@@ -595,28 +595,43 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
   }
 }
 
-// Sliding-window verify in one pass: at most 128 committed keys (window <= 129), at most 32 query
-// columns per workgroup (a column chunk of the G*T columns of (b, g)) and at most 4 new tokens, or
-// 8 with EXT (block drafts), bf16 (the ring workloads' shape). Wave w owns
-// committed-key block w (keys s0 + 32 w ..), so each column's maximum over all keys is known after
-// one exchange and no running max is needed:
-//   1. every wave forms S^T of its block and its column maxima; wave w also scores new tokens w
-//      and w + 4 on the VALU; maxima and new-token scores meet in LDS;
+// Sliding-window verify in one pass: at most 128 committed keys (window <= 129), NCB column
+// blocks of 32 query columns per workgroup (a column chunk of the G*T columns of (b, g); NCB = 2
+// serves 8 heads x 8 tokens in one workgroup) and at most 4 new tokens, or 8 with EXT (block
+// drafts), bf16 (the ring workloads' shape). Wave w owns committed-key block w (keys s0 + 32 w ..),
+// so each column's maximum over all keys is known after one exchange and no running max is needed:
+//   1. every wave forms S^T of its block for every column block (each K fragment feeds NCB
+//      products) and its column maxima; wave w also scores new tokens w and w + 4 on the VALU;
+//      maxima and new-token scores meet in LDS;
 //   2. every wave exponentiates its block against the common maximum and leaves P (bf16 MFMA
 //      fragments, over the no longer needed Q^T rows) and its column sums in LDS;
-//   3. wave w forms dv rows 32 w .. 32 w + 31 of O^T from all four blocks' V tiles and P, adds
-//      the new tokens and the sink, and writes them.
+//   3. wave w forms dv rows 32 w .. 32 w + 31 of O^T from all four blocks' V tiles and P (each V^T
+//      fragment feeds NCB products), adds the new tokens and the sink, and writes them.
 // Against the general kernel this replaces the per-wave (m, l, acc) merge (64 KB of LDS traffic
-// and four barriers per workgroup) by two exchanges of 8 KB. A block past the committed keys
-// holds zero V rows and masked scores, so the products stay finite. Tokens 4..7 (EXT): LDS is full
-// during step 1, so their K rows are fetched into registers at kernel start and their V rows are
-// written after the first barrier next to the P fragments.
-template <bool ROPE, bool EXT>
+// and four barriers per workgroup) by two exchanges. A block past the committed keys holds zero V
+// rows and masked scores, so the products stay finite. Tokens 4..7 (EXT): LDS is full during
+// step 1, so their K rows are fetched into registers at kernel start and their V rows are written
+// after the first barrier next to the P fragments.
+template <int NCB>
+struct WindowLds {
+  using L = DecodeLds<BF16, NCB>;
+  static constexpr int kQBytes = L::kQBytes, kNewBytes = L::kNewBytes, kVBytes = L::kVBytes;
+  static constexpr int kWork = kDecNW * kVBytes;  // the four waves' V tiles
+  static constexpr int kX = NCB * 32 * 4;         // one [column block][column] fp32 row
+  // exchange: column maxima [wave][cb][col], new-token scores [token][cb][col], sums [wave][cb][col]
+  static constexpr int kXBytes = (kDecNW + 2 * kDecNW + kDecNW) * kX;
+  static constexpr int kBytes = kQBytes + kNewBytes + kWork + kXBytes;
+  static constexpr int kPBytes = kDecNW * 2 * NCB * 64 * 16;  // P fragments over the Q^T rows
+  static_assert(kPBytes + 4 * kDDV * 2 <= kQBytes, "P fragments and tokens 4..7's V rows fit the Q^T rows");
+};
+
+template <int NCB, bool ROPE, bool EXT>
 __global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_window_kernel(const DecodeArgs a) {
   using E = BF16;
-  using Lds = DecodeLds<E, 1>;
-  __shared__ __attribute__((aligned(16))) char smem[Lds::kBytes];
+  using Lds = DecodeLds<E, NCB>;
+  using W = WindowLds<NCB>;
+  __shared__ __attribute__((aligned(16))) char smem[W::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -680,7 +695,7 @@ void decode_window_kernel(const DecodeArgs a) {
 
   KeyRows<E> cur;
   {
-    QStage<E, 1, ROPE> st;
+    QStage<E, NCB, ROPE> st;
     st.load(a, tid, b, g, cbase, ncols, P);
     if (has_keys) {
       const int pos = min(key0 + col, s1 - 1);
@@ -697,12 +712,11 @@ void decode_window_kernel(const DecodeArgs a) {
     st.store(smem, tid, ncols, true, a.T);
   }
   char* sq = smem;
-  char* snew = smem + Lds::kQBytes;
-  char* work = snew + Lds::kNewBytes;
-  float* xm = reinterpret_cast<float*>(smem + (Lds::kBytes - kDecNW * 64 * 4 * 2));  // [wave][col]
-  float* xs = xm + kDecNW * 32;                                                      // [token][col], 8 tokens
-  float* xl = xs + 2 * kDecNW * 32;                                                  // [wave][col]
-  static_assert(4 * kDecNW * 32 * 4 <= kDecNW * 64 * 4 * 2, "exchange area");
+  char* snew = smem + W::kQBytes;
+  char* work = snew + W::kNewBytes;
+  float* xm = reinterpret_cast<float*>(work + W::kWork);  // [wave][cb][col]
+  float* xs = xm + kDecNW * NCB * 32;                     // [token][cb][col], 8 tokens
+  float* xl = xs + 2 * kDecNW * NCB * 32;                 // [wave][cb][col]
   __syncthreads();  // Q^T and the new-token rows are in LDS
   if constexpr (EXT && ROPE) {
     if (half == 0) {
@@ -711,120 +725,150 @@ void decode_window_kernel(const DecodeArgs a) {
     }
   }
 
-  const bool cvalid = col < ncols;
-  const int cg = cbase + col;              // column within the G*T columns of (b, g)
-  const int tq = cvalid ? cg % a.T : 0;   // new token of this column
+  bool cvalid[NCB];
+  int tq[NCB];  // new token of this lane's column in each column block
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    cvalid[cb] = cb * 32 + col < ncols;
+    tq[cb] = cvalid[cb] ? (cbase + cb * 32 + col) % a.T : 0;
+  }
   const float c = a.scale_log2;
 
-  // ---- 1. S^T of this wave's block, column maxima, new token `wave` ----
-  cur.store_v(work + wave * Lds::kVBytes, col, half);
-  f32x16 s = zero16();
+  // ---- 1. S^T of this wave's block, column maxima, new tokens `wave` and `wave + 4` ----
+  cur.store_v(work + wave * W::kVBytes, col, half);
+  f32x16 s[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) s[cb] = zero16();
 #pragma unroll
   for (int kk = 0; kk < kDDQK / 16; ++kk) {
-    const bf16x8 qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                            sq + (col * Lds::kQStride + 16 * kk + 8 * half) * E::kBytes));
-    s = mma(cur.kfrag(kk), qf, s);
-  }
-  float bmax = -INFINITY;
+    const bf16x8 kf = cur.kfrag(kk);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int pos = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
-    s[r] = (pos < s1 && P + tq - pos < a.window) ? s[r] * c : -INFINITY;
-    bmax = fmaxf(bmax, s[r]);
-  }
-  bmax = halves_max(bmax);
-  if (half == 0) xm[wave * 32 + col] = bmax;
-  // score of new token t for this lane's column: q . k over this half's 96 elements (K chunks from
-  // `krow` in LDS, or from registers for tokens 4..7), then across halves
-  auto new_score = [&](int t, const char* krow, bool in_regs) {
-    const char* qrow = sq + col * Lds::kQStride * E::kBytes;
-    float dot = 0.f;
-#pragma unroll
-    for (int i = 0; i < kHalfChunks; ++i) {
-      const int e0 = (kDDQK / 2) * half + E::kPerChunk * i;
-      const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + e0 * E::kBytes);
-      const u32x4 kv = in_regs ? kx[EXT ? i : 0] : *reinterpret_cast<const u32x4*>(krow + e0 * E::kBytes);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dot = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[j]), as_bf16x2(kv[j]), dot, false);
+    for (int cb = 0; cb < NCB; ++cb) {
+      const bf16x8 qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                              sq + ((cb * 32 + col) * Lds::kQStride + 16 * kk + 8 * half) * E::kBytes));
+      s[cb] = mma(kf, qf, s[cb]);
     }
-    dot = halves_sum(dot);
-    const bool vis = cvalid && tq >= t && tq - t < a.window;
-    if (half == 0) xs[t * 32 + col] = vis ? dot * c : -INFINITY;
+  }
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int pos = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      s[cb][r] = (pos < s1 && P + tq[cb] - pos < a.window) ? s[cb][r] * c : -INFINITY;
+      bmax = fmaxf(bmax, s[cb][r]);
+    }
+    bmax = halves_max(bmax);
+    if (half == 0) xm[(wave * NCB + cb) * 32 + col] = bmax;
+  }
+  // score of new token t for this lane's column of every column block: q . k over this half's 96
+  // elements (K chunks from `krow` in LDS, or from registers for tokens 4..7), then across halves
+  auto new_score = [&](int t, const char* krow, bool in_regs) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const char* qrow = sq + (cb * 32 + col) * Lds::kQStride * E::kBytes;
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < kHalfChunks; ++i) {
+        const int e0 = (kDDQK / 2) * half + E::kPerChunk * i;
+        const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + e0 * E::kBytes);
+        const u32x4 kv = in_regs ? kx[EXT ? i : 0] : *reinterpret_cast<const u32x4*>(krow + e0 * E::kBytes);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dot = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[j]), as_bf16x2(kv[j]), dot, false);
+      }
+      dot = halves_sum(dot);
+      const bool vis = cvalid[cb] && tq[cb] >= t && tq[cb] - t < a.window;
+      if (half == 0) xs[(t * NCB + cb) * 32 + col] = vis ? dot * c : -INFINITY;
+    }
   };
   if (wave < a.T) new_score(wave, snew + wave * kDDQK * E::kBytes, false);
   if (EXT && tok_hi < a.T) new_score(tok_hi, nullptr, true);
   __syncthreads();  // maxima and new-token scores are in LDS; Q^T is no longer read
 
   // ---- 2. P of this block against the common maximum ----
-  const int head = cvalid ? a.hl.at(g * a.G + cg / a.T) : 0;
-  const float sink_l2 = (a.sink && cvalid) ? a.sink[head] * kLog2e : -INFINITY;
-  float M = sink_l2;
-#pragma unroll
-  for (int w = 0; w < kDecNW; ++w) M = fmaxf(M, xm[w * 32 + col]);
   constexpr int kNT = EXT ? 2 * kDecNW : kDecNW;  // new tokens this instance handles
-  float snt[kNT];
+  float M[NCB], sink_l2[NCB], snt[kNT][NCB];
+  int head[NCB];
+  char* sp = sq;  // P fragments [block][ks][cb][lane], 16 bytes each, over the Q^T rows
 #pragma unroll
-  for (int t = 0; t < kNT; ++t) {
-    snt[t] = t < a.T ? xs[t * 32 + col] : -INFINITY;
-    M = fmaxf(M, snt[t]);
+  for (int cb = 0; cb < NCB; ++cb) {
+    head[cb] = cvalid[cb] ? a.hl.at(g * a.G + (cbase + cb * 32 + col) / a.T) : 0;
+    sink_l2[cb] = (a.sink && cvalid[cb]) ? a.sink[head[cb]] * kLog2e : -INFINITY;
+    M[cb] = sink_l2[cb];
+#pragma unroll
+    for (int w = 0; w < kDecNW; ++w) M[cb] = fmaxf(M[cb], xm[(w * NCB + cb) * 32 + col]);
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+      snt[t][cb] = t < a.T ? xs[(t * NCB + cb) * 32 + col] : -INFINITY;
+      M[cb] = fmaxf(M[cb], snt[t][cb]);
+    }
+    const float M_use = (M[cb] == -INFINITY) ? 0.f : M[cb];
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[cb][r] = fast_exp2(s[cb][r] - M_use);
+      rs += s[cb][r];
+    }
+    rs = halves_sum(rs);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      st16(sp + (((wave * 2 + ks) * NCB + cb) * 64 + lane) * 16, __builtin_bit_cast(u32x4, frag_from_acc<E>(s[cb], 8 * ks)));
+    if (half == 0) xl[(wave * NCB + cb) * 32 + col] = rs;
   }
-  const float M_use = (M == -INFINITY) ? 0.f : M;
-  float rs = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s[r] = fast_exp2(s[r] - M_use);
-    rs += s[r];
-  }
-  rs = halves_sum(rs);
-  char* sp = sq;  // P fragments [block][ks][lane], 16 bytes each, over the Q^T rows
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    st16(sp + ((wave * 2 + ks) * 64 + lane) * 16, __builtin_bit_cast(u32x4, frag_from_acc<E>(s, 8 * ks)));
-  if (half == 0) xl[wave * 32 + col] = rs;
   // V rows of tokens 4..7 next to the P fragments, in the part of the Q^T rows P leaves free
-  char* snew_hi = sq + kDecNW * 2 * 64 * 16;
-  static_assert(kDecNW * 2 * 64 * 16 + 4 * kDDV * 2 <= Lds::kQBytes, "tokens 4..7 fit beside P");
+  char* snew_hi = sq + W::kPBytes;
   if (EXT && tid < nvx) st16(snew_hi + tid * 16, vx);
   __syncthreads();  // P fragments, block sums and the V rows of tokens 4..7 are in LDS
 
   // ---- 3. dv rows 32 wave .. 32 wave + 31 of O^T over all blocks, new tokens, sink ----
-  f32x16 acc = zero16();
+  f32x16 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero16();
 #pragma unroll
   for (int kb = 0; kb < kDecNW; ++kb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, ld16(sp + ((kb * 2 + ks) * 64 + lane) * 16));
-      acc = mma(vt_frag_tr(work + kb * Lds::kVBytes, Lds::kVStride, wave, ks, lane), pf, acc);
+      const bf16x8 vf = vt_frag_tr(work + kb * W::kVBytes, Lds::kVStride, wave, ks, lane);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, ld16(sp + (((kb * 2 + ks) * NCB + cb) * 64 + lane) * 16));
+        acc[cb] = mma(vf, pf, acc[cb]);
+      }
     }
-  float L = a.sink && cvalid ? fast_exp2(sink_l2 - M_use) : 0.f;
 #pragma unroll
-  for (int w = 0; w < kDecNW; ++w) L += xl[w * 32 + col];
+  for (int cb = 0; cb < NCB; ++cb) {
+    const float M_use = (M[cb] == -INFINITY) ? 0.f : M[cb];
+    float L = a.sink && cvalid[cb] ? fast_exp2(sink_l2[cb] - M_use) : 0.f;
 #pragma unroll
-  for (int t = 0; t < kNT; ++t) {
-    if (t >= a.T) break;
-    const float pn = fast_exp2(snt[t] - M_use);
-    L += pn;
-    const char* vrow = t < 4 ? snew + Lds::kNewKBytes + t * kDDV * E::kBytes : snew_hi + (t - 4) * kDDV * E::kBytes;
+    for (int w = 0; w < kDecNW; ++w) L += xl[(w * NCB + cb) * 32 + col];
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+      if (t >= a.T) break;
+      const float pn = fast_exp2(snt[t][cb] - M_use);
+      L += pn;
+      const char* vrow = t < 4 ? snew + Lds::kNewKBytes + t * kDDV * E::kBytes : snew_hi + (t - 4) * kDDV * E::kBytes;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const u32x2 w2 = *reinterpret_cast<const u32x2*>(vrow + (32 * wave + 8 * gq + 4 * half) * 2);
+        acc[cb][4 * gq + 0] = __builtin_fmaf(pn, __uint_as_float(w2[0] << 16), acc[cb][4 * gq + 0]);
+        acc[cb][4 * gq + 1] = __builtin_fmaf(pn, __uint_as_float(w2[0] & 0xFFFF0000u), acc[cb][4 * gq + 1]);
+        acc[cb][4 * gq + 2] = __builtin_fmaf(pn, __uint_as_float(w2[1] << 16), acc[cb][4 * gq + 2]);
+        acc[cb][4 * gq + 3] = __builtin_fmaf(pn, __uint_as_float(w2[1] & 0xFFFF0000u), acc[cb][4 * gq + 3]);
+      }
+    }
+    if (!cvalid[cb]) continue;
+    const float inv = 1.f / L;
+    char* orow = (char*)a.o + (((size_t)b * a.T + tq[cb]) * a.Hq + head[cb]) * kDDV * E::kBytes;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const u32x2 w2 = *reinterpret_cast<const u32x2*>(vrow + (32 * wave + 8 * gq + 4 * half) * 2);
-      acc[4 * gq + 0] = __builtin_fmaf(pn, __uint_as_float(w2[0] << 16), acc[4 * gq + 0]);
-      acc[4 * gq + 1] = __builtin_fmaf(pn, __uint_as_float(w2[0] & 0xFFFF0000u), acc[4 * gq + 1]);
-      acc[4 * gq + 2] = __builtin_fmaf(pn, __uint_as_float(w2[1] << 16), acc[4 * gq + 2]);
-      acc[4 * gq + 3] = __builtin_fmaf(pn, __uint_as_float(w2[1] & 0xFFFF0000u), acc[4 * gq + 3]);
+      u32x2 w2;
+      w2[0] = pack_bf16x2(acc[cb][4 * gq] * inv, acc[cb][4 * gq + 1] * inv);
+      w2[1] = pack_bf16x2(acc[cb][4 * gq + 2] * inv, acc[cb][4 * gq + 3] * inv);
+      *reinterpret_cast<u32x2*>(orow + (32 * wave + 8 * gq + 4 * half) * 2) = w2;
     }
+    if (a.lse && wave == 0 && half == 0)
+      a.lse[((size_t)b * a.T + tq[cb]) * a.Hq + head[cb]] = (M[cb] + fast_log2(L)) * kLn2;
   }
-  if (!cvalid) return;
-  const float inv = 1.f / L;
-  char* orow = (char*)a.o + (((size_t)b * a.T + tq) * a.Hq + head) * kDDV * E::kBytes;
-#pragma unroll
-  for (int gq = 0; gq < 4; ++gq) {
-    u32x2 w2;
-    w2[0] = pack_bf16x2(acc[4 * gq] * inv, acc[4 * gq + 1] * inv);
-    w2[1] = pack_bf16x2(acc[4 * gq + 2] * inv, acc[4 * gq + 3] * inv);
-    *reinterpret_cast<u32x2*>(orow + (32 * wave + 8 * gq + 4 * half) * 2) = w2;
-  }
-  if (a.lse && wave == 0 && half == 0) a.lse[((size_t)b * a.T + tq) * a.Hq + head] = (M + fast_log2(L)) * kLn2;
 }
 
 // Folds the split partials and the sink (once) into O and LSE. A workgroup covers kCombCols query
@@ -941,10 +985,10 @@ size_t decode_ws_bytes(int B, int Hkv, int ncols, int nsplit) {
   return (size_t)B * Hkv * nsplit * ncols_pad * kRec * sizeof(float);
 }
 
-// The one-pass window kernel serves a single split of at most four 32-key blocks with at most 32
-// query columns per workgroup and at most 8 new tokens.
+// The one-pass window kernel serves a single split of at most four 32-key blocks with at most
+// 64 query columns per workgroup and at most 8 new tokens.
 static bool window_kernel_fits(const DecodeArgs& a) {
-  const bool cols = a.ncols <= 32 || a.chunk_cols == 32;  // every workgroup's chunk fits one column block
+  const bool cols = a.chunk_cols <= 2 * 32;  // every workgroup's chunk fits two column blocks
   return a.nsplit == 1 && a.keys_per_split <= 32 * kDecNW && cols && a.T <= 2 * kDecNW;
 }
 
@@ -958,10 +1002,15 @@ static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t str
   const dim3 grid(a.nsplit, a.Hkv * a.n_chunks, a.B);
   const dim3 block(kDecNW * 64);
   if (bf16 && window_kernel_fits(a)) {
-    if (a.T > kDecNW)
-      hipLaunchKernelGGL((decode_window_kernel<ROPE, true>), grid, block, 0, stream, a);
+    const bool two = (a.n_chunks > 1 ? a.chunk_cols : a.ncols) > 32;
+    if (two && a.T > kDecNW)
+      hipLaunchKernelGGL((decode_window_kernel<2, ROPE, true>), grid, block, 0, stream, a);
+    else if (two)
+      hipLaunchKernelGGL((decode_window_kernel<2, ROPE, false>), grid, block, 0, stream, a);
+    else if (a.T > kDecNW)
+      hipLaunchKernelGGL((decode_window_kernel<1, ROPE, true>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_window_kernel<ROPE, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_window_kernel<1, ROPE, false>), grid, block, 0, stream, a);
     return;
   }
   const bool two = (a.n_chunks > 1 ? a.chunk_cols : a.ncols) > 32;
