@@ -286,7 +286,9 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_len, window: int, max_cache_
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
     keep, kvm = _kv_map(kv_map, Hq)
-    if workspace == "static":  # the library's static scratch: nothing is allocated
+    if isinstance(workspace, str):  # "static": the library's static scratch, nothing is allocated
+        if workspace != "static":
+            raise ValueError(f"workspace: a tensor, None or 'static' (got {workspace!r})")
         if rope is not None:
             raise ValueError("the static-scratch decode takes rotated q / k_new (rope=None)")
         rc = library().mimo_attn_decode_noalloc(dt, B, T, Hq, Hkv, dqk, dv, _ptr(q), _ptr(k_new),
