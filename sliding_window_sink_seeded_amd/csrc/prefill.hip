@@ -652,7 +652,6 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   }
   wait_all();
   __syncthreads();
-  if constexpr (ROPE) rotate_q(qf, t0);  // later tiles' Q: at the end of the tile before
 
   KVStager<E, NT, 32, ROPE ? kRopeLds : kRopeNone> st;
   st.init(krow_stride, vrow_stride, tid);
@@ -672,12 +671,14 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
     // unconditional (on the last tile: this tile's block again, and one shared Q row, unused), so
     // that the compiler's wait counts see one straight-line sequence of loads and stores.
     st.load(kbase, vbase, krow_stride, vrow_stride, 32 * min(t + 1, t1 - 1), a.L, tid);
-    u32x4 tchunk;  // RoPE: this thread's share of the table rows of tile t + 2
-    if constexpr (ROPE) tchunk = table_chunk(kQT * min(t + 2, t1 - 1));
     const char* qrow_next = has_next ? qbase + (size_t)min(p0 + kQT + col, a.L - 1) * qrow_stride : qbase;
 #pragma unroll
     for (int kk = 0; kk < kDQK / 16; ++kk) qn[kk] = global_q_frag<E>(qrow_next, kk, half);
     __builtin_amdgcn_sched_barrier(0);  // left alone, the scheduler sinks the Q loads below the MFMAs
+
+    // RoPE: this tile's Q is rotated here, where it is first needed (rotating the next tile's Q at
+    // the end of this one would hold the output stores until that Q had arrived)
+    if constexpr (ROPE) rotate_q(qc, t);
 
     // scores of the whole window: block j holds keys 32 * (t - NB + 1 + j) ..
     f32x16 s[NB];
@@ -737,10 +738,11 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
           acc[db] = mma(lds_vt_frag<E, 32>(smem + base[j] + Tile::kKBytes, db, ks, lane), pf[j][ks],
                         acc[db]);
 
-    // RoPE: the next tile's Q has arrived by now; rotate it here, off the next tile's path
-    if constexpr (ROPE) {
-      if (has_next) rotate_q(qn, t + 1);
-    }
+    // RoPE: this thread's share of the table rows of tile t + 2 (written to LDS below), requested
+    // only after the PV products are issued: held across the tile, its four registers spilled and
+    // the spill store waited for the load
+    u32x4 tchunk;
+    if constexpr (ROPE) tchunk = table_chunk(kQT * min(t + 2, t1 - 1));
 
     // ring update first, output stores last: the stores drain under the barrier and the next
     // tile's score MFMAs instead of holding up the loads that reuse their registers
