@@ -243,27 +243,31 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
 #ifndef MIMO_GA_PINGPONG
 #define MIMO_GA_PINGPONG 1
 #endif
+#ifndef MIMO_GA_BK
+#define MIMO_GA_BK 96
+#endif
 #ifndef MIMO_GA_DEPTH
-#define MIMO_GA_DEPTH 4
+#define MIMO_GA_DEPTH 2
 #endif
 #ifndef MIMO_GA_SGB
 #define MIMO_GA_SGB 1
 #endif
-#ifndef MIMO_GA_PRIO
-#define MIMO_GA_PRIO 0
-#endif
 //
 // bf16 global attention with 8 query heads per workgroup (wave w = head w of the chunk, all on the
-// same 32 query rows; waves w and w + 4 share a SIMD). Each wave alternates MFMA phases
-// M_k = [O^T += V^T P^T of block k - 1, S^T = K Q^T of block k] and softmax phases V_k (masking,
-// running max, exponentials, P to bf16 fragments, rescale). Waves 0-3 (group A) run one phase
-// ahead of waves 4-7 (group B), so on every SIMD one wave issues MFMAs while the other works on
-// the VALU; a barrier closes every phase ("slot"):
+// same 32 query rows; waves w and w + 4 share a SIMD), over key blocks of BK keys. Each wave
+// alternates MFMA phases M_k = [O^T += V^T P^T of block k - 1, S^T = K Q^T of block k] and softmax
+// phases V_k (masking, running max, exponentials, P to bf16 fragments, rescale). Waves 0-3
+// (group A) run one phase ahead of waves 4-7 (group B), so on every SIMD one wave issues MFMAs
+// while the other works on the VALU; a barrier closes every phase ("slot"):
 //     slot 2k:   A runs M_k,  B runs V_{k-1}          slot 2k + 1:  A runs V_k,  B runs M_k
 // With n blocks there are 2n + 2 slots, and every wave passes the same 2n + 3 barriers (one after
-// the prologue). Block b is read in slots 2b .. 2b + 3, so three LDS stages rotate: block b + 1 is
-// loaded into registers at the start of slot 2b and stored, into the stage block b - 2 held, at
-// the end of slot 2b + 1, two slots of latency later.
+// the prologue). K of block k and V of block k - 1 are read in exactly slots 2k and 2k + 1, so they
+// share stage k % 2 of two LDS stages; the stage that they overwrite was read last in slot 2k - 3
+// (K) or 2k - 1 (V). Staging is global -> LDS (no registers) and happens in softmax phases, which
+// read no LDS: group B fetches K of block k + 1 in slot 2k (its V_{k-1}), group A fetches V of
+// block k in slot 2k + 1 (its V_k); each waits for its loads before the barrier that closes the
+// slot. (The compiler makes a wave's LDS reads wait for all of its loads that target LDS, so loads
+// issued before an MFMA phase would stall it.)
 // Scheduling-group pattern of an M phase (masks: 0x100 LDS reads, 0x008 MFMA): the reads of the
 // first D operand fragments, then product i followed by the reads of fragment i + D. Fragments of
 // the first NPV products (V^T) take two transposing reads, the others (K) one.
@@ -283,12 +287,15 @@ struct GaReadAhead {
   }
 };
 
-template <int ROPE>
+template <int ROPE, int BK>
 __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a) {
   using E = BF16;
-  using Tile = PrefillTile<E, 64>;
+  using Tile = PrefillTile<E, BK>;
   using Frag = bf16x8;
-  constexpr int NW = 8, BK = 64, NS = 3;
+  constexpr int NW = 8, NS = 2;
+  constexpr int NKB = BK / 32;  // 32-key MFMA row blocks of a key block
+  constexpr int NKS = BK / 16;  // 16-key slices (PV contraction steps)
+  static_assert(BK % 32 == 0 && NS * Tile::kStageBytes <= 160 * 1024, "two stages fit LDS");
   __shared__ __attribute__((aligned(16))) char smem[NS * Tile::kStageBytes];
 
   const int tid = threadIdx.x;
@@ -318,17 +325,26 @@ __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a
   const char* kbase = (const char*)a.k + ((size_t)b * a.L * a.Hkv + g) * kDQK * 2;
   const char* vbase = (const char*)a.v + ((size_t)b * a.L * a.Hkv + g) * kDV * 2;
 
-  // K/V blocks are staged through registers (global loads, later LDS stores), not loaded straight
-  // into LDS: the compiler makes every LDS read of a wave wait for all of its loads that target LDS
-  // (it cannot tell the stages apart), which would stall the next MFMA phase on the prefetch.
-  KVStager<E, 512, BK> st;
-  st.init(krow_stride, vrow_stride, tid);
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    if (j < n) {
-      st.load(kbase, vbase, krow_stride, vrow_stride, j * BK, a.L, tid);
-      st.store(smem + j * Tile::kStageBytes, tid);
-    }
+  // group B (waves 4-7) stages K, group A (waves 0-3) stages V
+  const int gw = wave & 3;
+  using KDma = RowsDMA<4, BK, Tile::kKStride * 2 / 16, kDQK / 8>;
+  using VDma = RowsDMA<4, BK, Tile::kVStride * 2 / 16, kDV / 8>;
+  static_assert(KDma::kChunks * 16 == Tile::kKBytes && VDma::kChunks * 16 == Tile::kVBytes, "regions tile the stage");
+  uint32_t doff[KDma::kPer > VDma::kPer ? KDma::kPer : VDma::kPer];
+  auto stage_k = [&](int kb) {  // K of block kb into stage kb % 2 (group B)
+    KDma::load(doff, smem + (kb % NS) * Tile::kStageBytes, kbase, krow_stride, kb * BK, a.L, gw, lane);
+  };
+  auto stage_v = [&](int kb) {  // V of block kb into stage (kb + 1) % 2 (group A)
+    VDma::load(doff, smem + ((kb + 1) % NS) * Tile::kStageBytes + Tile::kKBytes, vbase, vrow_stride, kb * BK, a.L,
+               gw, lane);
+  };
+  if (grp == 0) {
+    VDma::init(doff, vrow_stride, gw, lane);
+    stage_v(0);
+  } else {
+    KDma::init(doff, krow_stride, gw, lane);
+    stage_k(0);
+    if (n > 1) stage_k(1);
   }
   Frag qf[kDQK / 16];
   {
@@ -353,10 +369,10 @@ __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a
   f32x16 acc[kDV / 32];
 #pragma unroll
   for (int db = 0; db < kDV / 32; ++db) acc[db] = zero16();
-  f32x16 s[2];
-  Frag pf[BK / 16];
+  f32x16 s[NKB];
+  Frag pf[NKS];
 #pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) pf[ks] = Frag{};
+  for (int ks = 0; ks < NKS; ++ks) pf[ks] = Frag{};
 
   wait_vm();
   __syncthreads();
@@ -373,14 +389,11 @@ __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a
   // operand fragment is read D products ahead of its use.
   auto mphase = [&](int k, auto pv_tag, auto qk_tag) {
     constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
-#if MIMO_GA_PRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
-    constexpr int NPV = PV ? 16 : 0, NM = NPV + (QK ? 24 : 0), D = MIMO_GA_DEPTH;
-    // this lane's addresses in the stages of blocks k - 1 (V) and k (K); every fragment is then at
-    // a constant offset from them (the LDS read's offset field). The empty asm keeps the compiler
-    // from re-associating them into one hoisted register per fragment.
-    uint32_t vb = lds_base + ((k + NS - 1) % NS) * Tile::kStageBytes + Tile::kKBytes + vt_lane;
+    constexpr int NPV = PV ? 4 * NKS : 0, NM = NPV + (QK ? NKB * (kDQK / 16) : 0), D = MIMO_GA_DEPTH;
+    // this lane's addresses in the stage of pair k (V of block k - 1, K of block k); every
+    // fragment is then at a constant offset from them (the LDS read's offset field). The empty asm
+    // keeps the compiler from re-associating them into one hoisted register per fragment.
+    uint32_t vb = lds_base + (k % NS) * Tile::kStageBytes + Tile::kKBytes + vt_lane;
     uint32_t kb = lds_base + (k % NS) * Tile::kStageBytes + k_lane;
     asm volatile("" : "+v"(vb), "+v"(kb));
     auto frag = [&](int i) -> Frag {  // A operand of product i
@@ -396,8 +409,8 @@ __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a
         u[4] = y[0]; u[5] = y[1]; u[6] = y[2]; u[7] = y[3];
         return __builtin_bit_cast(bf16x8, u);
       }
-      const int j = i - NPV;
-      const uint32_t a0 = kb + (32 * (j % 2) * Tile::kKStride + 16 * (j / 2)) * 2;
+      const int j = i - NPV;  // score product j: key rows 32 (j % NKB), dims 16 (j / NKB)
+      const uint32_t a0 = kb + (32 * (j % NKB) * Tile::kKStride + 16 * (j / NKB)) * 2;
       return __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)a0);
     };
     Frag buf[D];
@@ -405,8 +418,8 @@ __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a
     for (int i = 0; i < D; ++i)
       if (i < NM) buf[i] = frag(i);
     if constexpr (QK) {
-      s[0] = zero16();
-      s[1] = zero16();
+#pragma unroll
+      for (int sb = 0; sb < NKB; ++sb) s[sb] = zero16();
     }
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
@@ -416,15 +429,12 @@ __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a
         acc[i % 4] = mma(x, pf[i / 4], acc[i % 4]);
       } else {
         const int j = i - NPV;
-        s[j % 2] = mma(x, qf[j / 2], s[j % 2]);
+        s[j % NKB] = mma(x, qf[j / NKB], s[j % NKB]);
       }
     }
 #if MIMO_GA_SGB
     // keep that order: the first D fragments' reads, then one product and the next reads, ...
     GaReadAhead<NPV, NM, D, 0>::emit();
-#endif
-#if MIMO_GA_PRIO
-    __builtin_amdgcn_s_setprio(0);
 #endif
   };
 
@@ -433,7 +443,7 @@ __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a
     constexpr bool MASKED = decltype(masked_tag)::value;
     float bmax = -INFINITY;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    for (int sb = 0; sb < NKB; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if constexpr (MASKED) {
@@ -457,7 +467,7 @@ __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a
     const float m_use = (m == -INFINITY) ? 0.f : m;
     float rs = 0.f;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    for (int sb = 0; sb < NKB; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(__builtin_fmaf(s[sb][r], c, -m_use));
@@ -467,7 +477,7 @@ __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a
     }
     l += halves_sum(rs);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) pf[ks] = frag_from_acc<E>(s[ks >> 1], 8 * (ks & 1));
+    for (int ks = 0; ks < NKS; ++ks) pf[ks] = frag_from_acc<E>(s[ks >> 1], 8 * (ks & 1));
   };
 
   // barrier that closes a slot
@@ -476,29 +486,22 @@ __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // block kb + 1 is loaded into registers at the start of slot 2 kb and stored into the stage of
-  // block kb - 2 (read last in slot 2 kb - 1) at the end of slot 2 kb + 1, by every wave
-  auto load_at = [&](int kb) {
-    if (kb >= 2 && kb + 1 < n) st.load(kbase, vbase, krow_stride, vrow_stride, (kb + 1) * BK, a.L, tid);
-  };
-  auto store_at = [&](int kb) {
-    if (kb >= 2 && kb + 1 < n) st.store(smem + ((kb + 1) % NS) * Tile::kStageBytes, tid);
-  };
   const std::false_type no{};
   const std::true_type yes{};
   if (grp == 0) {
     mphase(0, no, yes);
     close_slot();                          // slot 0
     for (int k = 0; k + 1 < n; ++k) {
+      if (k >= 1) stage_v(k);
       vphase(k, no);
-      store_at(k);
+      wait_vm();
       close_slot();                        // slot 2k + 1
-      load_at(k + 1);
       mphase(k + 1, yes, yes);
       close_slot();                        // slot 2k + 2
     }
+    if (n > 1) stage_v(n - 1);
     vphase(n - 1, yes);
-    store_at(n - 1);
+    wait_vm();
     close_slot();                          // slot 2n - 1
     mphase(n, yes, no);
     close_slot();                          // slot 2n
@@ -508,11 +511,11 @@ __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a
     mphase(0, no, yes);
     close_slot();                          // slot 1
     for (int k = 0; k + 1 < n; ++k) {
-      load_at(k + 1);
+      if (k + 2 < n) stage_k(k + 2);
       vphase(k, no);
+      wait_vm();
       close_slot();                        // slot 2k + 2
       mphase(k + 1, yes, yes);
-      store_at(k + 1);
       close_slot();                        // slot 2k + 3
     }
     vphase(n - 1, yes);
@@ -819,9 +822,9 @@ static hipError_t launch_global(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(rope_k_kernel<BF16>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, a);
     PrefillArgs r = a;
     r.k = a.k_ws;
-    hipLaunchKernelGGL(prefill_global_kernel<kPreRopeQ>, dim3((unsigned)n_wg), dim3(512), 0, stream, r);
+    hipLaunchKernelGGL((prefill_global_kernel<kPreRopeQ, MIMO_GA_BK>), dim3((unsigned)n_wg), dim3(512), 0, stream, r);
   } else {
-    hipLaunchKernelGGL(prefill_global_kernel<kPreRopeNone>, dim3((unsigned)n_wg), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((prefill_global_kernel<kPreRopeNone, MIMO_GA_BK>), dim3((unsigned)n_wg), dim3(512), 0, stream, a);
   }
   return hipGetLastError();
 }

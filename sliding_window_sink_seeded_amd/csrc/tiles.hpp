@@ -244,6 +244,55 @@ struct KVStagerDMA {
   }
 };
 
+// Global -> LDS staging (16-byte global_load_lds) of ROWS consecutive rows of one bf16 tensor into
+// a padded LDS region of RC 16-byte chunks per row (the first DC of them data), by a group of NWG
+// waves: instruction u covers region chunks 64 u .. 64 u + 63 and is issued by wave u % NWG of the
+// group. A lane whose chunk is padding re-reads a data chunk of its row; in the last instruction
+// the lanes past the region are switched off. Rows at or past L are read from row L - 1. The caller
+// waits for the loads (vmcnt) before the barrier that publishes the region. The caller also holds
+// the lane's offsets (off[i]: byte offset of its chunk in instruction i from row 0 of the block),
+// so that wave groups staging different tensors can share one register array.
+template <int NWG, int ROWS, int RC, int DC>
+struct RowsDMA {
+  static constexpr int kChunks = ROWS * RC;
+  static constexpr int kInst = (kChunks + 63) / 64;
+  static constexpr int kPer = (kInst + NWG - 1) / NWG;  // instructions per wave (at most)
+
+  __device__ static int row_chunk(int u, int lane, int& ch) {
+    const int p = min(64 * u + lane, kChunks - 1);
+    ch = min(p % RC, DC - 1);
+    return p / RC;
+  }
+  __device__ __forceinline__ static void init(uint32_t* off, size_t stride, int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int ch;
+      const int row = row_chunk(min(w + i * NWG, kInst - 1), lane, ch);
+      off[i] = (uint32_t)(row * stride + ch * 16);
+    }
+  }
+  // Issues wave w's loads of rows row0 .. row0 + ROWS - 1 into `region`; only a block that reaches
+  // past L needs each lane's row again (a uniform branch around it).
+  __device__ __forceinline__ static void load(const uint32_t* off, char* region, const char* base, size_t stride,
+                                              int row0, int L, int w, int lane) {
+    const bool tail = row0 + ROWS > L;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = w + i * NWG;
+      if (u >= kInst) break;  // uniform per wave
+      const char* p = base + (size_t)row0 * stride + off[i];
+      if (tail) {
+        int ch;
+        const int row = row_chunk(u, lane, ch);
+        p += ((size_t)min(row0 + row, L - 1) - (row0 + row)) * stride;
+      }
+      if (kChunks % 64 == 0 || u < kInst - 1 || 64 * u + lane < kChunks)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)p,
+                                         (__attribute__((address_space(3))) void*)(region + 1024 * u), 16, 0, 0);
+    }
+  }
+};
+
 // Waits for this wave's outstanding global loads, including global -> LDS loads (vmcnt 0; expcnt
 // and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
