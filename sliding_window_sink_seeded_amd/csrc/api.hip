@@ -418,7 +418,9 @@ int decode_impl(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
   // columns takes chunks of 32: the one-block kernel keeps two waves per SIMD, which beats
   // reading the short K/V history once with the 64-column kernel (8 heads x 8 tokens: 107 vs
   // 147 us).
-  a.chunk_cols = (plan.nsplit == 1 && a.ncols > 32) ? kChunkCols1Split : mimo::kMaxCols;
+  // fp32 always takes chunks of 32: its 64-column kernel needs more than the 512 registers of a
+  // lane (the K and V half rows alone are 160) and spilled.
+  a.chunk_cols = (dt == MIMO_F32 || (plan.nsplit == 1 && a.ncols > 32)) ? kChunkCols1Split : mimo::kMaxCols;
   // bf16 single passes over at most four 32-key blocks run the one-pass window kernel, which
   // takes two column blocks per workgroup (each K / V fragment then feeds two products)
   if (dt == MIMO_BF16 && plan.nsplit == 1 && plan.keys_per_split <= 128 && a.ncols > 32)

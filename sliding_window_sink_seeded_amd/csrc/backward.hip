@@ -561,7 +561,9 @@ size_t backward_ws_bytes(int B, int L, int Hq) {
 
 template <typename E>
 static hipError_t launch_backward(BackwardArgs a, hipStream_t stream) {
-  constexpr int NW = 8, BK = 32;
+  // dQ workgroups of 8 waves (bf16) or 4 (fp32: at 8 waves, two per SIMD, its operands need more
+  // than the 256 registers a wave then has, and spilled)
+  constexpr int NW = E::kBytes == 2 ? 8 : 4, BK = 32;
   // dK/dV workgroups of 4 waves (128 keys) walk every query tile that sees any of their keys; under
   // a short window each wave sees only some of them (5 of 8 at W = 128) and computes the rest with
   // p = 0. Two-wave workgroups (64 keys, two per CU) walk 6 tiles for the same 5 (bf16; the fp32

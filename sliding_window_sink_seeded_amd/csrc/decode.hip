@@ -1018,9 +1018,7 @@ static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t str
     hipLaunchKernelGGL((decode_kernel<BF16, 2, true, ROPE>), grid, block, 0, stream, a);
   else if (bf16)
     hipLaunchKernelGGL((decode_kernel<BF16, 1, kPrefetch1Col, ROPE>), grid, block, 0, stream, a);
-  else if (two)
-    hipLaunchKernelGGL((decode_kernel<F32, 2, false, ROPE>), grid, block, 0, stream, a);
-  else
+  else  // fp32: column chunks of 32
     hipLaunchKernelGGL((decode_kernel<F32, 1, false, ROPE>), grid, block, 0, stream, a);
 }
 

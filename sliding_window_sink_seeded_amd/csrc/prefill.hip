@@ -287,10 +287,19 @@ struct GaReadAhead {
   }
 };
 
+// LDS stage of the ping-pong kernel: K rows [BK][192 + 8], then V rows [BK][128 + 16] (bf16; the
+// padding keeps the K rows' 16-byte reads on distinct banks)
+template <int BK>
+struct GaTile {
+  static constexpr int kKStride = kDQK + 8, kVStride = kDV + 16;
+  static constexpr int kKBytes = BK * kKStride * 2, kVBytes = BK * kVStride * 2;
+  static constexpr int kStageBytes = kKBytes + kVBytes;
+};
+
 template <int ROPE, int BK>
 __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a) {
   using E = BF16;
-  using Tile = PrefillTile<E, BK>;
+  using Tile = GaTile<BK>;
   using Frag = bf16x8;
   constexpr int NW = 8, NS = 2;
   constexpr int NKB = BK / 32;  // 32-key MFMA row blocks of a key block
