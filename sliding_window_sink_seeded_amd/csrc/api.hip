@@ -425,6 +425,10 @@ int decode_impl(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
   // takes two column blocks per workgroup (each K / V fragment then feeds two products)
   if (dt == MIMO_BF16 && plan.nsplit == 1 && plan.keys_per_split <= 128 && a.ncols > 32)
     a.chunk_cols = kWindowCols;
+  // other bf16 calls with more than 64 columns (16 heads x 8 tokens) run the column-split kernel,
+  // 128 columns per workgroup, which streams the cache once for all of them
+  else if (dt == MIMO_BF16 && a.ncols > mimo::kMaxCols)
+    a.chunk_cols = mimo::kColsCols;
   a.n_chunks = (a.ncols + a.chunk_cols - 1) / a.chunk_cols;
   if ((long long)a.Hkv * a.n_chunks > 65535) return fail(MIMO_EUNSUPPORTED, "too many KV heads x column chunks");
   if (int rc = group_heads(Hq, Hkv, kv_head_of_q, &a.hl)) return rc;

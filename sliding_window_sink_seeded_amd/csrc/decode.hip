@@ -871,6 +871,260 @@ void decode_window_kernel(const DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------ column-split decode (many query columns)
+//
+// Decode with more than 64 query columns per KV head (16 heads x 8 tokens of a global layer) in one
+// pass over the cache. Wave w owns query columns 32 w .. 32 w + 31 of the workgroup's chunk of
+// 128, and the four waves share every 32-key block of K and V in LDS (two stages). Per block each
+// wave forms S^T = K Q^T of its columns (K fragments from LDS, Q^T fragments in registers), runs
+// the online softmax of its columns and adds V^T P^T (V^T read transposed from LDS): every cached
+// byte is read from HBM once for all 128 columns, and the accumulators of a wave stay at 64
+// registers. Blocks are staged through registers two blocks ahead: block i + 2 is requested
+// before block i's math, block i + 1 (requested a block earlier) is written to LDS after it.
+// (Global -> LDS loads into three stages were slower: the compiler could not tell the stages apart
+// for one of the three and made that block's LDS reads wait for every fetch in flight.) The last
+// split then takes the T new tokens as one more block (rotated on the way with RoPE). No merge
+// between waves: each writes its own columns' O (one split: sink folded, LSE) or split records for
+// combine_kernel.
+struct ColsTile {
+  static constexpr int kKStride = kDDQK + 8, kVStride = kDDV + 16;  // bf16 per LDS row (padded)
+  static constexpr int kKBytes = 32 * kKStride * 2, kStageBytes = kKBytes + 32 * kVStride * 2;
+  // staging: thread t moves row t / 8 of the block, K chunks 3 (t % 8) .. +2 and V chunks
+  // 2 (t % 8) .. +1 (16-byte chunks; 24 per K row, 16 per V row)
+  static constexpr int kKPer = kDDQK / 8 / 8, kVPer = kDDV / 8 / 8;
+};
+
+struct ColsRegs {
+  u32x4 k[ColsTile::kKPer], v[ColsTile::kVPer];
+};
+
+// Requests thread tid's chunks of the 32-key block at key0 (keys past s1 - 1 read key s1 - 1,
+// masked later); position p is in slot (p + off) mod C.
+__device__ __forceinline__ void cols_load(ColsRegs& r, const char* kc, const char* vc, size_t kstride,
+                                          size_t vstride, size_t row0, int key0, int s1, int off, int C,
+                                          int tid) {
+  const int row = min(tid >> 3, s1 - 1 - key0), q = tid & 7;
+  int slot = (key0 + row + off) % C;
+  slot += slot < 0 ? C : 0;
+  const char* kp = kc + (row0 + slot) * kstride + q * ColsTile::kKPer * 16;
+  const char* vp = vc + (row0 + slot) * vstride + q * ColsTile::kVPer * 16;
+#pragma unroll
+  for (int i = 0; i < ColsTile::kKPer; ++i) r.k[i] = ld16(kp + 16 * i);
+#pragma unroll
+  for (int i = 0; i < ColsTile::kVPer; ++i) r.v[i] = ld16(vp + 16 * i);
+}
+
+__device__ __forceinline__ void cols_store(char* stage, const ColsRegs& r, int tid) {
+  const int row = tid >> 3, q = tid & 7;
+  char* kd = stage + row * ColsTile::kKStride * 2 + q * ColsTile::kKPer * 16;
+  char* vd = stage + ColsTile::kKBytes + row * ColsTile::kVStride * 2 + q * ColsTile::kVPer * 16;
+#pragma unroll
+  for (int i = 0; i < ColsTile::kKPer; ++i) st16(kd + 16 * i, r.k[i]);
+#pragma unroll
+  for (int i = 0; i < ColsTile::kVPer; ++i) st16(vd + 16 * i, r.v[i]);
+}
+
+template <bool ROPE>
+__global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_cols_kernel(
+    const DecodeArgs a) {
+  using E = BF16;
+  using T = ColsTile;
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::kStageBytes];
+  char* const st0 = smem;
+  char* const st1 = smem + T::kStageBytes;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int split = blockIdx.x;
+  const int chunk = blockIdx.y % a.n_chunks;
+  const int g = blockIdx.y / a.n_chunks;
+  const int b = blockIdx.z;
+  const int cbase = chunk * a.chunk_cols;
+  const int ncols = min(a.chunk_cols, a.ncols - cbase);
+
+  int P = a.cache_len[b];
+  P = P < 0 ? 0 : (P > a.max_len ? a.max_len : P);
+  const int off = a.cache_offset ? a.cache_offset[b] : 0;
+  const int list0 = max(0, P - a.window + 1);
+  const int s0 = list0 + split * a.keys_per_split;
+  const int s1 = min(P, s0 + a.keys_per_split);
+  const int nb = s1 > s0 ? (s1 - s0 + 31) / 32 : 0;
+
+  const size_t krow_bytes = (size_t)kDDQK * 2, vrow_bytes = (size_t)kDDV * 2;
+  const char* kc = (const char*)a.k_cache + (size_t)g * krow_bytes;
+  const char* vc = (const char*)a.v_cache + (size_t)g * vrow_bytes;
+  const size_t kstride = (size_t)a.Hkv * krow_bytes, vstride = (size_t)a.Hkv * vrow_bytes;
+  const size_t row0 = (size_t)b * a.C;
+
+  // this lane's query column (padding columns load a valid row and are never written)
+  const int cl = 32 * wave + col;
+  const bool cvalid = cl < ncols;
+  const int c = cbase + min(cl, ncols - 1);
+  const int t = c % a.T;
+  const int head = a.hl.at(g * a.G + c / a.T);
+  const int qpos = P + t;
+
+  // the first two blocks' requests, then the Q^T fragments (rotated at position P + t with RoPE)
+  ColsRegs r0, r1;
+  if (nb > 0) cols_load(r0, kc, vc, kstride, vstride, row0, s0, s1, off, a.C, tid);
+  if (nb > 1) cols_load(r1, kc, vc, kstride, vstride, row0, s0 + 32, s1, off, a.C, tid);
+  bf16x8 qf[kDDQK / 16];
+  {
+    const char* qrow = (const char*)a.q + (((size_t)b * a.T + t) * a.Hq + head) * krow_bytes;
+#pragma unroll
+    for (int kk = 0; kk < kDDQK / 16; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, ld16(qrow + (16 * kk + 8 * half) * 2));
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float cs[16];
+        rope_load<8>(a.rope, qpos, 16 * kk + 8 * half, cs);
+        rope_rotate_frag<E>(qf[kk], qf[kk + 2], cs);
+      }
+    }
+  }
+  if (nb > 0) cols_store(st0, r0, tid);
+  __syncthreads();
+
+  const float c2 = a.scale_log2;
+  float m = -INFINITY, l = 0.f;
+  f32x16 acc[kDDV / 32];
+#pragma unroll
+  for (int db = 0; db < kDDV / 32; ++db) acc[db] = zero16();
+
+  // one 32-key block from `stage`: vis(k) says whether key row k (0..31) is visible to this lane's
+  // column (only called when the block is not wholly visible)
+  auto block = [&](const char* stage, bool full, auto vis) {
+    f32x16 s = zero16();
+#pragma unroll
+    for (int kk = 0; kk < kDDQK / 16; ++kk) {
+      const bf16x8 kf = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(stage + (col * T::kKStride + 16 * kk + 8 * half) * 2));
+      s = mma(kf, qf[kk], s);
+    }
+    if (!full) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = vis(8 * (r >> 2) + 4 * half + (r & 3)) ? s[r] : -INFINITY;
+    }
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[r]);
+    const float mb = halves_max(bmax) * c2;
+    // lazy running max (log2 units): rescale only when a candidate exceeds it by more than 8
+    if (__builtin_amdgcn_ballot_w64(mb > m + 8.f || (m == -INFINITY && mb > m)) != 0) {
+      const float m_new = fmaxf(m, mb);
+      const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.f : m_new));
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDDV / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      m = m_new;
+    }
+    const float m_use = (m == -INFINITY) ? 0.f : m;
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(__builtin_fmaf(s[r], c2, -m_use));
+      s[r] = p;
+      rs += p;
+    }
+    l += halves_sum(rs);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pf = frag_from_acc<E>(s, 8 * ks);
+#pragma unroll
+      for (int db = 0; db < kDDV / 32; ++db)
+        acc[db] = mma(vt_frag_tr(stage + T::kKBytes, T::kVStride, db, ks, lane), pf, acc[db]);
+    }
+  };
+
+  // committed keys: step i requests block i + 2 into the register set that held block i, does
+  // block i's math, writes block i + 1 into the other stage (free: read in step i - 1) and closes
+  // with a barrier; the register sets and stages alternate, so the loop runs two steps per trip
+  auto step = [&](int i, const char* cur, char* other, ColsRegs& mine, const ColsRegs& next) {
+    if (i + 2 < nb) cols_load(mine, kc, vc, kstride, vstride, row0, s0 + 32 * (i + 2), s1, off, a.C, tid);
+    __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the math
+    const int key0 = s0 + 32 * i;
+    const bool full = key0 + 32 <= s1 && P + a.T - 1 - key0 < a.window;
+    block(cur, full, [&](int k) { return key0 + k < s1 && qpos - (key0 + k) < a.window; });
+    if (i + 1 < nb) cols_store(other, next, tid);
+    __syncthreads();
+  };
+  for (int i = 0; i < nb; i += 2) {
+    step(i, st0, st1, r0, r1);
+    if (i + 1 < nb) step(i + 1, st1, st0, r1, r0);
+  }
+
+  // new tokens (last split): rows 0..T-1 of a block hold their K and V (rotated at P + tn with
+  // RoPE), rows T..31 zeros; laid out 40 chunks (24 K, 16 V) per row on consecutive threads, so a
+  // row's rotated chunks and their partners share one wave
+  if (split == a.nsplit - 1) {
+    __syncthreads();  // every wave is done with the stages
+    constexpr int kKCh = kDDQK / 8, kRow = kKCh + kDDV / 8;
+    for (int u = tid; u < 32 * kRow; u += kColsNW * 64) {  // same trip count in every lane
+      const int r = u / kRow, ch = u % kRow;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (r < a.T)
+        x = ch < kKCh ? ld16((const char*)a.k_new + (((size_t)b * a.T + r) * a.Hkv + g) * krow_bytes + ch * 16)
+                      : ld16((const char*)a.v_new + (((size_t)b * a.T + r) * a.Hkv + g) * vrow_bytes + (ch - kKCh) * 16);
+      if constexpr (ROPE) {
+        constexpr int H = kRopeH<E>;
+        float cs[16];
+        const bool rot = r < a.T && ch < 2 * H;
+        if (rot) rope_load<8>(a.rope, P + r, (ch % H) * 8, cs);
+        x = rope_chunk_xlane<E>(x, rot ? ch : 2 * H, lane, cs);
+      }
+      if (ch < kKCh)
+        st16(st0 + (r * T::kKStride) * 2 + ch * 16, x);
+      else
+        st16(st0 + T::kKBytes + (r * T::kVStride) * 2 + (ch - kKCh) * 16, x);
+    }
+    __syncthreads();
+    block(st0, false, [&](int k) { return k < a.T && k <= t && t - k < a.window; });
+  }
+
+  if (!cvalid) return;
+  if (a.nsplit == 1) {
+    const float s_l2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
+    const float M = fmaxf(m, s_l2);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    const float w = fast_exp2(m - M_use);
+    const float L = l * w + (a.sink ? fast_exp2(s_l2 - M_use) : 0.f);
+    const float sc = w / L;
+    char* orow = (char*)a.o + (((size_t)b * a.T + t) * a.Hq + head) * vrow_bytes;
+#pragma unroll
+    for (int db = 0; db < kDDV / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w2;
+        w2[0] = pack_bf16x2(acc[db][4 * j] * sc, acc[db][4 * j + 1] * sc);
+        w2[1] = pack_bf16x2(acc[db][4 * j + 2] * sc, acc[db][4 * j + 3] * sc);
+        *reinterpret_cast<u32x2*>(orow + (32 * db + 8 * j + 4 * half) * 2) = w2;
+      }
+    if (a.lse && half == 0) a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(L)) * kLn2;
+  } else {
+    // split record of column c: unnormalised acc against this split's max m, and l
+    const int ncols_pad = ((a.ncols + 31) / 32) * 32;
+    float* rec = a.ws + ((((size_t)b * a.Hkv + g) * a.nsplit + split) * ncols_pad + c) * kRec;
+#pragma unroll
+    for (int db = 0; db < kDDV / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 w4;
+        w4[0] = acc[db][4 * j]; w4[1] = acc[db][4 * j + 1]; w4[2] = acc[db][4 * j + 2]; w4[3] = acc[db][4 * j + 3];
+        *reinterpret_cast<f32x4*>(rec + 32 * db + 8 * j + 4 * half) = w4;
+      }
+    if (half == 0) {
+      rec[kDDV] = m;
+      rec[kDDV + 1] = l;
+    }
+  }
+}
+
 // Folds the split partials and the sink (once) into O and LSE. A workgroup covers kCombCols query
 // columns of one (b, g); thread (column, quad) owns 4 consecutive dv of that column. Pass 1 takes
 // the max over the splits' m, pass 2 sums the rescaled l and acc, kCombUnroll splits at a time so
@@ -1001,6 +1255,10 @@ template <bool ROPE>
 static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.nsplit, a.Hkv * a.n_chunks, a.B);
   const dim3 block(kDecNW * 64);
+  if (bf16 && a.chunk_cols == kColsCols) {
+    hipLaunchKernelGGL(decode_cols_kernel<ROPE>, grid, dim3(kColsNW * 64), 0, stream, a);
+    return;
+  }
   if (bf16 && window_kernel_fits(a)) {
     const bool two = (a.n_chunks > 1 ? a.chunk_cols : a.ncols) > 32;
     if (two && a.T > kDecNW)

@@ -6,6 +6,8 @@
 namespace mimo {
 
 constexpr int kMaxCols = 64;  // decode: query columns per workgroup (query heads per KV head x new tokens)
+constexpr int kColsNW = 4;    // column-split decode: waves per workgroup, 32 query columns each
+constexpr int kColsCols = 32 * kColsNW;
 constexpr int kMaxNew = 8;    // decode: new tokens per sequence (next token + drafts)
 
 // Prefill arguments (kernel argument block, passed by value).

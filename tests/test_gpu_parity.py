@@ -240,6 +240,28 @@ def test_decode_global_splits(dtype, num_splits):
     check_decode(inp, 2100, num_splits=num_splits)
 
 
+@pytest.mark.parametrize("T,num_splits", [(8, 1), (8, 2), (8, 7), (8, 0), (5, 0), (5, 3)])
+def test_decode_many_columns(T, num_splits):
+    # 16 heads x 5..8 tokens = 80..128 query columns per KV head: the column-split kernel (one
+    # workgroup of four 32-column waves sharing each staged K/V block); with T = 5 the last 48
+    # columns are padding. Lengths: empty, inside the first block, ragged, a full cache.
+    say(f"decode many columns T={T} splits={num_splits}")
+    inp = decode_inputs(51 + T + num_splits, 4, T, 64, 4, 192, 128, 2100, 10**9, "bf16",
+                        ring_offsets=False, len_range=(0, 1))
+    inp.cache_len = np.array([0, 17, 1333, 2100], np.int32)
+    check_decode(inp, 2100, num_splits=num_splits)
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 0])
+def test_decode_many_columns_ring(num_splits):
+    # the same kernel over a ring of 1000 slots (window 1000) at every kind of offset: the keys of a
+    # block wrap around the end of the ring
+    say(f"decode many columns, ring, splits={num_splits}")
+    inp = decode_inputs(58 + num_splits, 6, 8, 32, 2, 192, 128, 1000, 1000, "bf16", len_range=(0, 1))
+    inp.cache_len = np.array([0, 40, 999, 1000, 1017, 4321], np.int32)
+    check_decode(inp, 4321, num_splits=num_splits)
+
+
 def test_decode_split_results_agree():
     say("decode split agreement")
     inp = decode_inputs(42, 2, 4, 64, 4, 192, 128, 5000, 10**9, "bf16", ring_offsets=False,
