@@ -425,8 +425,9 @@ int decode_impl(mimo_dtype dt, int B, int T, int Hq, int Hkv, int d_qk, int d_v,
   // takes two column blocks per workgroup (each K / V fragment then feeds two products)
   if (dt == MIMO_BF16 && plan.nsplit == 1 && plan.keys_per_split <= 128 && a.ncols > 32)
     a.chunk_cols = kWindowCols;
-  // other bf16 calls with more than 64 columns (16 heads x 8 tokens) run the column-split kernel,
-  // 128 columns per workgroup, which streams the cache once for all of them
+  // other bf16 calls with more than 64 columns (16 heads x 8 tokens) run the column-split kernel
+  // with 128 columns per workgroup, which streams the cache once for all of them (33..64 columns
+  // run it with 64)
   else if (dt == MIMO_BF16 && a.ncols > mimo::kMaxCols)
     a.chunk_cols = mimo::kColsCols;
   a.n_chunks = (a.ncols + a.chunk_cols - 1) / a.chunk_cols;

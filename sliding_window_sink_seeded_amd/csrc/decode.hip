@@ -15,21 +15,22 @@
 // fifth, nearly empty block on one wave.
 //
 // Work decomposition: one workgroup per (split, KV head g, column chunk, sequence b). The G*T query
-// columns of (b, g) - every query head of the group times every new token - are the MFMA columns
-// (32 per column block, at most two blocks per workgroup; more columns, e.g. 16 heads x 8 tokens,
-// are cut into chunks of 64 that run as separate workgroups), so each K/V element read from HBM
-// serves all the columns of a chunk; Q^T sits in LDS, shared by the waves. The split's keys are cut into 32-key blocks dealt round-robin to the waves. Lane
-// (col, half) of a wave fetches half of the K row and half of the V row of key key0 + col: the K
-// half is directly its MFMA A fragment, the V half goes to a wave-private LDS tile that the PV
-// product reads back transposed.
-// The next block's fetch is issued before the current block's math (register double buffer).
-// A wave keeps an online softmax per column (no sink here), then the waves of the workgroup
-// merge through LDS in a fixed order:
-//   * single pass (one split): the sink joins the merge and O / LSE are written;
-//   * several splits: the merged, unnormalised (m, l, acc) go to the workspace and
-//     combine_kernel folds the splits and the sink (counted once) into O / LSE.
-// Keys past the end of the split are fetched from its last key (finite data, masked to weight 0).
-// The running max is refreshed lazily (see update_max).
+// columns of (b, g) - every query head of the group times every new token - are the MFMA columns,
+// so each K/V element read from HBM serves all the columns of a chunk. Three kernels:
+//   * decode_window_kernel: bf16 single passes over at most four 32-key blocks (the 128-slot ring
+//     of a sliding-window layer), one block per wave, 32 or 64 columns per workgroup;
+//   * decode_cols_kernel: other bf16 calls with more than 32 columns (64 or 128 per workgroup):
+//     the waves split the columns and share each 32-key block staged in LDS;
+//   * decode_kernel: 32 columns per workgroup (bf16 up to 32 columns, fp32 in chunks of 32). Q^T
+//     sits in LDS, shared by the waves; the split's keys are cut into 32-key blocks dealt
+//     round-robin to the waves. Lane (col, half) of a wave fetches half of the K row and half of
+//     the V row of key key0 + col: the K half is directly its MFMA A fragment, the V half goes to
+//     a wave-private LDS tile that the PV product reads back transposed. A wave keeps an online
+//     softmax per column (no sink here), then the waves merge through LDS in a fixed order.
+// Single pass (one split): the sink is folded in and O / LSE are written. Several splits: the
+// unnormalised (m, l, acc) of each column go to the workspace and combine_kernel folds the splits
+// and the sink (counted once) into O / LSE. Keys past the end of a split are fetched from its last
+// key (finite data, masked to weight 0). Running maxima are refreshed lazily (see update_max).
 #include "launch.hpp"
 
 namespace mimo {
@@ -873,9 +874,10 @@ void decode_window_kernel(const DecodeArgs a) {
 
 // ------------------------------------------------------ column-split decode (many query columns)
 //
-// Decode with more than 64 query columns per KV head (16 heads x 8 tokens of a global layer) in one
-// pass over the cache. Wave w owns query columns 32 w .. 32 w + 31 of the workgroup's chunk of
-// 128, and the four waves share every 32-key block of K and V in LDS (two stages). Per block each
+// Decode with more than 32 query columns per KV head (16 heads x 4 or x 8 tokens of a global layer)
+// in one pass over the cache. With 128 columns per workgroup, wave w owns query columns
+// 32 w .. 32 w + 31; with 64, waves w and w + 2 share column block w and split the dv rows. The
+// four waves share every 32-key block of K and V in LDS (two stages). Per block each
 // wave forms S^T = K Q^T of its columns (K fragments from LDS, Q^T fragments in registers), runs
 // the online softmax of its columns and adds V^T P^T (V^T read transposed from LDS): every cached
 // byte is read from HBM once for all 128 columns, and the accumulators of a wave stay at 64
@@ -924,11 +926,16 @@ __device__ __forceinline__ void cols_store(char* stage, const ColsRegs& r, int t
   for (int i = 0; i < ColsTile::kVPer; ++i) st16(vd + 16 * i, r.v[i]);
 }
 
-template <bool ROPE>
+// NCB column blocks of 32 per workgroup: 4 (128 columns, each wave all 128 dv rows of its block)
+// or 2 (64 columns: waves w and w + 2 share column block w and take dv rows 0..63 and 64..127;
+// both form the block's scores).
+template <int NCB, bool ROPE>
 __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_cols_kernel(
     const DecodeArgs a) {
   using E = BF16;
   using T = ColsTile;
+  static_assert(NCB == 4 || NCB == 2, "128 or 64 columns per workgroup");
+  constexpr int NDB = (kDDV / 32) * NCB / kColsNW;  // dv blocks of 32 per wave
   __shared__ __attribute__((aligned(16))) char smem[2 * T::kStageBytes];
   char* const st0 = smem;
   char* const st1 = smem + T::kStageBytes;
@@ -960,8 +967,10 @@ __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2)
   const size_t kstride = (size_t)a.Hkv * krow_bytes, vstride = (size_t)a.Hkv * vrow_bytes;
   const size_t row0 = (size_t)b * a.C;
 
-  // this lane's query column (padding columns load a valid row and are never written)
-  const int cl = 32 * wave + col;
+  // this lane's query column (padding columns load a valid row and are never written) and the
+  // wave's dv blocks db0 .. db0 + NDB - 1
+  const int cl = 32 * (wave % NCB) + col;
+  const int db0 = NDB * (wave / NCB);
   const bool cvalid = cl < ncols;
   const int c = cbase + min(cl, ncols - 1);
   const int t = c % a.T;
@@ -991,9 +1000,9 @@ __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2)
 
   const float c2 = a.scale_log2;
   float m = -INFINITY, l = 0.f;
-  f32x16 acc[kDDV / 32];
+  f32x16 acc[NDB];
 #pragma unroll
-  for (int db = 0; db < kDDV / 32; ++db) acc[db] = zero16();
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
 
   // one 32-key block from `stage`: vis(k) says whether key row k (0..31) is visible to this lane's
   // column (only called when the block is not wholly visible)
@@ -1019,9 +1028,9 @@ __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2)
       const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.f : m_new));
       l *= alpha;
 #pragma unroll
-      for (int db = 0; db < kDDV / 32; ++db)
+      for (int d = 0; d < NDB; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
       m = m_new;
     }
     const float m_use = (m == -INFINITY) ? 0.f : m;
@@ -1037,8 +1046,8 @@ __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2)
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 pf = frag_from_acc<E>(s, 8 * ks);
 #pragma unroll
-      for (int db = 0; db < kDDV / 32; ++db)
-        acc[db] = mma(vt_frag_tr(stage + T::kKBytes, T::kVStride, db, ks, lane), pf, acc[db]);
+      for (int d = 0; d < NDB; ++d)
+        acc[d] = mma(vt_frag_tr(stage + T::kKBytes, T::kVStride, db0 + d, ks, lane), pf, acc[d]);
     }
   };
 
@@ -1097,28 +1106,28 @@ __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2)
     const float sc = w / L;
     char* orow = (char*)a.o + (((size_t)b * a.T + t) * a.Hq + head) * vrow_bytes;
 #pragma unroll
-    for (int db = 0; db < kDDV / 32; ++db)
+    for (int d = 0; d < NDB; ++d)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         u32x2 w2;
-        w2[0] = pack_bf16x2(acc[db][4 * j] * sc, acc[db][4 * j + 1] * sc);
-        w2[1] = pack_bf16x2(acc[db][4 * j + 2] * sc, acc[db][4 * j + 3] * sc);
-        *reinterpret_cast<u32x2*>(orow + (32 * db + 8 * j + 4 * half) * 2) = w2;
+        w2[0] = pack_bf16x2(acc[d][4 * j] * sc, acc[d][4 * j + 1] * sc);
+        w2[1] = pack_bf16x2(acc[d][4 * j + 2] * sc, acc[d][4 * j + 3] * sc);
+        *reinterpret_cast<u32x2*>(orow + (32 * (db0 + d) + 8 * j + 4 * half) * 2) = w2;
       }
-    if (a.lse && half == 0) a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(L)) * kLn2;
+    if (a.lse && half == 0 && db0 == 0) a.lse[((size_t)b * a.T + t) * a.Hq + head] = (M + fast_log2(L)) * kLn2;
   } else {
     // split record of column c: unnormalised acc against this split's max m, and l
     const int ncols_pad = ((a.ncols + 31) / 32) * 32;
     float* rec = a.ws + ((((size_t)b * a.Hkv + g) * a.nsplit + split) * ncols_pad + c) * kRec;
 #pragma unroll
-    for (int db = 0; db < kDDV / 32; ++db)
+    for (int d = 0; d < NDB; ++d)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f32x4 w4;
-        w4[0] = acc[db][4 * j]; w4[1] = acc[db][4 * j + 1]; w4[2] = acc[db][4 * j + 2]; w4[3] = acc[db][4 * j + 3];
-        *reinterpret_cast<f32x4*>(rec + 32 * db + 8 * j + 4 * half) = w4;
+        w4[0] = acc[d][4 * j]; w4[1] = acc[d][4 * j + 1]; w4[2] = acc[d][4 * j + 2]; w4[3] = acc[d][4 * j + 3];
+        *reinterpret_cast<f32x4*>(rec + 32 * (db0 + d) + 8 * j + 4 * half) = w4;
       }
-    if (half == 0) {
+    if (half == 0 && db0 == 0) {
       rec[kDDV] = m;
       rec[kDDV + 1] = l;
     }
@@ -1256,7 +1265,7 @@ static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t str
   const dim3 grid(a.nsplit, a.Hkv * a.n_chunks, a.B);
   const dim3 block(kDecNW * 64);
   if (bf16 && a.chunk_cols == kColsCols) {
-    hipLaunchKernelGGL(decode_cols_kernel<ROPE>, grid, dim3(kColsNW * 64), 0, stream, a);
+    hipLaunchKernelGGL((decode_cols_kernel<4, ROPE>), grid, dim3(kColsNW * 64), 0, stream, a);
     return;
   }
   if (bf16 && window_kernel_fits(a)) {
@@ -1271,9 +1280,10 @@ static void launch_decode_kernel(bool bf16, const DecodeArgs& a, hipStream_t str
       hipLaunchKernelGGL((decode_window_kernel<1, ROPE, false>), grid, block, 0, stream, a);
     return;
   }
+  // bf16 with 33..64 columns: the column-split kernel (2 column blocks, dv halves per wave)
   const bool two = (a.n_chunks > 1 ? a.chunk_cols : a.ncols) > 32;
   if (bf16 && two)
-    hipLaunchKernelGGL((decode_kernel<BF16, 2, true, ROPE>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_cols_kernel<2, ROPE>), grid, dim3(kColsNW * 64), 0, stream, a);
   else if (bf16)
     hipLaunchKernelGGL((decode_kernel<BF16, 1, kPrefetch1Col, ROPE>), grid, block, 0, stream, a);
   else  // fp32: column chunks of 32
