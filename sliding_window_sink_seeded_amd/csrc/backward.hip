@@ -268,11 +268,24 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   const int col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // key blocks in ascending order: under causal attention the first ones see the most queries
-  const int kb = (int)(blockIdx.x / (a.B * a.Hkv));
+  // key blocks in ascending order: under causal attention the first ones see the most queries.
+  // Paired (global layers): workgroup p takes key block p, walking its query tiles from the last
+  // down, then key block n - 1 - p, walking its tiles from the first up. Every workgroup then has
+  // the same number of tiles (a generation starts and ends together), and at any moment the first
+  // walks of all running workgroups are on one tile and their second walks on another, so they
+  // share the Q / dO rows through L2. (Unpaired, a workgroup started when an earlier one finished
+  // walked out of phase with the rest and fetched its rows alone: 30 GB per 32768-row global
+  // launch.)
+  const int pk = (int)(blockIdx.x / (a.B * a.Hkv));
   const int rest = blockIdx.x % (a.B * a.Hkv);
   const int g = rest % a.Hkv;
   const int b = rest / a.Hkv;
+  constexpr bool kPairable = NW == 4 && E::kBytes == 2;  // the launcher pairs only these
+  const int n_items = kPairable && a.kv_pairs && a.n_kblocks - 1 - pk != pk ? 2 : 1;
+  for (int item = 0; item < n_items; ++item) {
+  const bool asc = item == 1;
+  const int kb = asc ? a.n_kblocks - 1 - pk : pk;
+  if (item == 1) __syncthreads();  // every wave is done with the stages of the first walk
   const int kb0 = kb * 32 * NW;
   const int kw0 = kb0 + 32 * wave;  // this wave's first key
   const int kpos = kw0 + col;       // this lane's key
@@ -310,13 +323,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   const int qt_last = last_q / kQT;
   constexpr int GS = 32 * NW / kQT;
   const int ng = (kb0 + 32 * NW - 1 + a.window - 1) / kQT / GS - kb + 1;  // window <= L
-  const bool alt = ng <= kDkdvMaxGroups;
+  const bool alt = !a.kv_pairs && ng <= kDkdvMaxGroups;
   const int kbm = kb % ng;
   const int nsteps = a.G * (alt ? ng * GS : ntiles);
   auto step_head = [&](int step) { return step % a.G; };
   auto step_row = [&](int step) {
     const int t = step / a.G;
-    if (!alt) return (qt_last - t) * kQT;
+    if (!alt) return (asc ? qt0 + t : qt_last - t) * kQT;
     const int ph = t / GS - kbm;
     const int m = kb + (ph < 0 ? ph + ng : ph);
     return (m * GS + GS - 1 - t % GS) * kQT;
@@ -480,8 +493,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   //
   // Steps whose tile every key of the workgroup sees in full need no mask: rows at or after the
   // block's last key (q0 >= kb0 + 32 NW - 1), inside the window of its first key, and before L.
-  // In the descending order (long windows) they form one run [s_a, s_b); the steps before (a
-  // partial last tile) and after it (the tiles on the diagonal) take the masked variant. Each loop
+  // In the descending or ascending order (long windows) they form one run [s_a, s_b); the steps
+  // outside it (the tiles on the diagonal, a partial last tile) take the masked variant. Each loop
   // stays free of branches.
   auto stage = [&](int step) { return smem + (step & 1) * St::kBytes; };
   int s_a = 0, s_b = 0;
@@ -492,8 +505,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
     if (lim >= 0) {
       const int t_hi = (int)min((long long)qt_last, lim / kQT);
       if (t_lo <= t_hi) {
-        s_a = (qt_last - t_hi) * a.G;
-        s_b = (qt_last - t_lo + 1) * a.G;
+        s_a = (asc ? t_lo - qt0 : qt_last - t_hi) * a.G;
+        s_b = (asc ? t_hi - qt0 + 1 : qt_last - t_lo + 1) * a.G;
       }
     }
   }
@@ -525,6 +538,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   char* dvrow = (char*)a.dv + krow * kDV * E::kBytes;
   store_out_row<E>(dkrow, acck, a.scale, half, kvalid);
   store_out_row<E>(dvrow, accv, 1.f, half, kvalid);
+  }
 }
 
 // ---------------------------------------------------------------------------- sink gradient
@@ -579,8 +593,11 @@ static hipError_t launch_backward(BackwardArgs a, hipStream_t stream) {
   a.n_kblocks = (a.L + 32 * nwk - 1) / (32 * nwk);
   a.n_qtiles = (a.L + kQT - 1) / kQT;
 
+  // global layers (the window covers the sequence): key blocks p and n_kblocks - 1 - p share a
+  // workgroup (see the kernel)
+  a.kv_pairs = E::kBytes == 2 && !kv2 && a.window >= a.L ? 1 : 0;
   const long long n_dq = (long long)a.n_qblocks * a.B * a.Hkv * a.n_hchunks;
-  const long long n_kv = (long long)a.n_kblocks * a.B * a.Hkv;
+  const long long n_kv = (long long)(a.kv_pairs ? (a.n_kblocks + 1) / 2 : a.n_kblocks) * a.B * a.Hkv;
   if (n_dq > 0x7fffffffLL || n_kv > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((bwd_dq_kernel<E, NW, BK>), dim3((unsigned)n_dq), dim3(NW * 64), 0, stream, a);
   if constexpr (E::kBytes == 2) {

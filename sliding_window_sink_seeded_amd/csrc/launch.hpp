@@ -80,6 +80,7 @@ struct BackwardArgs {
   int n_qblocks;        // dq kernel: query blocks per (b, g, head chunk)
   int n_hchunks;        // dq kernel: G / heads_per_wg
   int n_kblocks;        // dk/dv kernel: key blocks per (b, g)
+  int kv_pairs;         // dk/dv kernel: 1 = a workgroup takes key blocks p and n_kblocks - 1 - p
   int n_qtiles;         // ceil(L / 32)
   HeadList hl;
 };
