@@ -1,4 +1,6 @@
-"""Builds libmimo_attn.so (gfx950) from csrc/ with hipcc, in-tree next to this file.
+"""Builds libmimo_attn.so (gfx950) from csrc/ with hipcc, in-tree next to this file, and the
+checking variant libmimo_attn_poison.so (every kernel fills its LDS with NaN before it starts,
+see poison_lds in csrc/common.hpp), which only the tests load.
 
 Usage: python -m sliding_window_sink_seeded_amd.build [-v]
 """
@@ -14,6 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmimo_attn.so")
+LIB_POISON = os.path.join(HERE, "libmimo_attn_poison.so")
 SOURCES = ["api.hip", "prefill.hip", "decode.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -33,18 +36,19 @@ def _quiet(stderr: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compiles every source (always) and links the shared library; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
+    """Compiles every source (always), for the product library and its LDS-poisoning variant, and
+    links both; returns the product library's path."""
+    variants = [(LIB, OBJDIR, []), (LIB_POISON, os.path.join(OBJDIR, "poison"), ["-DMIMO_POISON_LDS=1"])]
     procs = []
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
-        objs.append(obj)
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
-                                            text=True)))
+    for lib, objdir, extra in variants:
+        os.makedirs(objdir, exist_ok=True)
+        for src in SOURCES:
+            obj = os.path.join(objdir, src.replace(".hip", ".o"))
+            cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                                text=True)))
     failed = []
     for src, p in procs:
         out, err = p.communicate()
@@ -55,12 +59,14 @@ def build(verbose: bool = False) -> str:
             print(err, file=sys.stderr)
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(f"--- {s}\n{e}" for s, e in failed))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + _quiet(r.stderr))
-    os.replace(tmp, LIB)
+    for lib, objdir, _ in variants:
+        objs = [os.path.join(objdir, src.replace(".hip", ".o")) for src in SOURCES]
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + _quiet(r.stderr))
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -51,6 +51,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
   constexpr int NT = NW * 64;
   constexpr int NSB = BK / 32;
   __shared__ __attribute__((aligned(16))) char smem[2 * Tile::kStageBytes];
+  poison_lds(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -261,6 +262,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
   constexpr int QPT = kDQK * E::kBytes / 16 / 8;  // 16-byte Q chunks per thread and row
   constexpr int OPT = kDV * E::kBytes / 16 / 8;   // 16-byte dO chunks per thread and row
   __shared__ __attribute__((aligned(16))) char smem[2 * St::kBytes];
+  poison_lds(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -545,6 +547,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BackwardArgs a)
 
 __global__ __launch_bounds__(256) void bwd_sink_kernel(const BackwardArgs a) {
   __shared__ float red[256];
+  poison_lds(red, sizeof(red));
   const int h = blockIdx.x, tid = threadIdx.x;
   const int n = a.B * a.n_qtiles;
   const float* p = a.sink_part + (size_t)h * n;

@@ -131,6 +131,22 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 // Waits until every outstanding memory operation of this wave has completed.
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Checking builds (MIMO_POISON_LDS=1, libmimo_attn_poison.so): every kernel first fills its LDS
+// with all-ones words (NaN as fp32 and as bf16) and waits at a barrier, so a read of LDS that the
+// workgroup has not written turns its results into NaN instead of reusing what an earlier
+// workgroup left there (a missing write, or a read that overtakes the write behind a missing
+// barrier). Product builds compile this to nothing.
+#ifndef MIMO_POISON_LDS
+#define MIMO_POISON_LDS 0
+#endif
+__device__ __forceinline__ void poison_lds(void* lds, int bytes) {
+  if constexpr (MIMO_POISON_LDS != 0) {
+    const u32x4 nan = {~0u, ~0u, ~0u, ~0u};
+    for (int i = (int)threadIdx.x; i < bytes / 16; i += (int)blockDim.x) st16((char*)lds + 16 * i, nan);
+    __syncthreads();
+  }
+}
 __device__ __forceinline__ u32x4 zero_chunk() {
   u32x4 z;
   z[0] = z[1] = z[2] = z[3] = 0u;

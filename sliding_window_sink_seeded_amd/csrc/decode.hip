@@ -239,6 +239,7 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
   using Frag = typename E::Frag;
   using Lds = DecodeLds<E, NCB>;
   __shared__ __attribute__((aligned(16))) char smem[Lds::kBytes];
+  poison_lds(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -633,6 +634,7 @@ void decode_window_kernel(const DecodeArgs a) {
   using Lds = DecodeLds<E, NCB>;
   using W = WindowLds<NCB>;
   __shared__ __attribute__((aligned(16))) char smem[W::kBytes];
+  poison_lds(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -937,6 +939,7 @@ __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2)
   static_assert(NCB == 4 || NCB == 2, "128 or 64 columns per workgroup");
   constexpr int NDB = (kDDV / 32) * NCB / kColsNW;  // dv blocks of 32 per wave
   __shared__ __attribute__((aligned(16))) char smem[2 * T::kStageBytes];
+  poison_lds(smem, sizeof(smem));
   char* const st0 = smem;
   char* const st1 = smem + T::kStageBytes;
 

@@ -46,6 +46,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   constexpr int NT = NW * 64;
   constexpr int NSB = BK / 32;  // 32-key sub-blocks per block
   __shared__ __attribute__((aligned(16))) char smem[2 * Tile::kStageBytes];
+  poison_lds(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -306,6 +307,7 @@ __global__ __launch_bounds__(512) void prefill_global_kernel(const PrefillArgs a
   constexpr int NKS = BK / 16;  // 16-key slices (PV contraction steps)
   static_assert(BK % 32 == 0 && NS * Tile::kStageBytes <= 160 * 1024, "two stages fit LDS");
   __shared__ __attribute__((aligned(16))) char smem[NS * Tile::kStageBytes];
+  poison_lds(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -553,6 +555,7 @@ __global__ __launch_bounds__(512) void prefill_swa_kernel(const PrefillArgs a) {
   constexpr int kHalfRot = kRopeDims / 2;
   constexpr int kTblBytes = kQT * kHalfRot * 2 * 4;
   __shared__ __attribute__((aligned(16))) char smem[R * Tile::kStageBytes + (ROPE ? 3 * kTblBytes : 0)];
+  poison_lds(smem, sizeof(smem));
   char* tables = smem + R * Tile::kStageBytes;
   auto table_of = [&](int tile) { return tables + (tile % 3) * kTblBytes; };
 
