@@ -41,8 +41,16 @@
 extern "C" {
 #endif
 
-/* Storage dtype shared by q, k, v, the caches and o. Softmax and accumulation are fp32 for both. */
-typedef enum { MIMO_F32 = 0, MIMO_BF16 = 1 } mimo_dtype;
+/* Storage dtype shared by q, k, v, the caches and o. Softmax and accumulation are fp32 for both.
+ * The two range markers are not dtypes (every entry point rejects them with MIMO_EUNSUPPORTED, as
+ * any other value); they give the type the range of an int, so that the library can examine an
+ * unknown value a caller passes without undefined behaviour. */
+typedef enum {
+  MIMO_F32 = 0,
+  MIMO_BF16 = 1,
+  MIMO_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  MIMO_DTYPE_RANGE_MAX_ = 2147483647
+} mimo_dtype;
 
 enum {
   MIMO_OK = 0,

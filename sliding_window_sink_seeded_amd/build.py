@@ -1,6 +1,9 @@
-"""Builds libmimo_attn.so (gfx950) from csrc/ with hipcc, in-tree next to this file, and the
-checking variant libmimo_attn_poison.so (every kernel fills its LDS with NaN before it starts,
-see poison_lds in csrc/common.hpp), which only the tests load.
+"""Builds libmimo_attn.so (gfx950) from csrc/ with hipcc, in-tree next to this file, and two
+checking variants that only the tests load: libmimo_attn_poison.so (every kernel fills its LDS
+with NaN before it starts, see poison_lds in csrc/common.hpp) and libmimo_attn_hostsan.so (the
+host code alone - validation, planning, error paths - built with AddressSanitizer and
+UndefinedBehaviorSanitizer: api.hip, where it all lives, compiled with host-side sanitizers and
+linked with the product objects of the kernel files; the test preloads the sanitizer runtime).
 
 Usage: python -m sliding_window_sink_seeded_amd.build [-v]
 """
@@ -17,6 +20,11 @@ CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmimo_attn.so")
 LIB_POISON = os.path.join(HERE, "libmimo_attn_poison.so")
+LIB_HOSTSAN = os.path.join(HERE, "libmimo_attn_hostsan.so")
+# sanitizers for the host compilation alone (each flag behind -Xarch_host)
+HOSTSAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer"]
+HOSTSAN_SOURCES = ["api.hip"]
 SOURCES = ["api.hip", "prefill.hip", "decode.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -38,11 +46,14 @@ def _quiet(stderr: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compiles every source (always), for the product library and its LDS-poisoning variant, and
     links both; returns the product library's path."""
-    variants = [(LIB, OBJDIR, []), (LIB_POISON, os.path.join(OBJDIR, "poison"), ["-DMIMO_POISON_LDS=1"])]
+    hostsan_dir = os.path.join(OBJDIR, "hostsan")
+    variants = [(LIB, OBJDIR, [], SOURCES),
+                (LIB_POISON, os.path.join(OBJDIR, "poison"), ["-DMIMO_POISON_LDS=1"], SOURCES),
+                (LIB_HOSTSAN, hostsan_dir, HOSTSAN_FLAGS, HOSTSAN_SOURCES)]
     procs = []
-    for lib, objdir, extra in variants:
+    for lib, objdir, extra, sources in variants:
         os.makedirs(objdir, exist_ok=True)
-        for src in SOURCES:
+        for src in sources:
             obj = os.path.join(objdir, src.replace(".hip", ".o"))
             cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
@@ -59,8 +70,9 @@ def build(verbose: bool = False) -> str:
             print(err, file=sys.stderr)
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(f"--- {s}\n{e}" for s, e in failed))
-    for lib, objdir, _ in variants:
-        objs = [os.path.join(objdir, src.replace(".hip", ".o")) for src in SOURCES]
+    for lib, objdir, _, sources in variants:
+        # a variant that compiles only some sources takes the product objects of the rest
+        objs = [os.path.join(objdir if src in sources else OBJDIR, src.replace(".hip", ".o")) for src in SOURCES]
         tmp = lib + ".tmp"
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
         r = subprocess.run(cmd, capture_output=True, text=True)
