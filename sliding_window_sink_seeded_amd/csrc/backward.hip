@@ -50,7 +50,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
   using Frag = typename E::Frag;
   constexpr int NT = NW * 64;
   constexpr int NSB = BK / 32;
-  __shared__ __attribute__((aligned(16))) char smem[2 * Tile::kStageBytes];
+  // bf16 blocks go global -> LDS directly (no staging registers), fp32 through registers
+  constexpr bool kDMA = E::kBytes == 2;
+  // bf16: a workgroup whose key blocks fit kAllStages stages (every sliding-window tile) fetches
+  // them all at the start and then runs them without waits or barriers; longer ranges (global
+  // layers) rotate two stages. (Two stages for all made each workgroup wait for a block's round
+  // trip five times after its prologue.)
+  constexpr int kAllStages = kDMA ? 6 : 2;
+  __shared__ __attribute__((aligned(16))) char smem[kAllStages * Tile::kStageBytes];
   poison_lds(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
@@ -94,6 +101,34 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
 #pragma unroll
     for (int kk = 0; kk < kDV / 16; ++kk) df[kk] = global_q_frag<E>(drow, kk, half);
   }
+  const float c = a.scale_log2;
+  f32x16 acc[kDQK / 32];
+#pragma unroll
+  for (int t = 0; t < kDQK / 32; ++t) acc[t] = zero16();
+
+  // the K/V blocks are requested before D is formed, so their latency overlaps that of O
+  const int K0 = max(0, P0 - a.window + 1);
+  const int kstart = (K0 / BK) * BK;
+  const int nblk = (P1 - kstart + BK - 1) / BK;
+  const bool all_blocks = kDMA && nblk <= kAllStages;  // uniform
+
+  KVStager<E, NT, BK, kRopeNone, kVRows> st;
+  KVStagerDMA<NW, BK, kVRows> dma;
+  if constexpr (kDMA) {
+    dma.init(krow_stride, vrow_stride, wave, lane);
+    if (all_blocks) {
+      for (int ib = 0; ib < nblk; ++ib)
+        dma.load(smem + ib * Tile::kStageBytes, kbase, vbase, krow_stride, vrow_stride, kstart + ib * BK, a.L,
+                 wave, lane);
+    } else {
+      dma.load(smem, kbase, vbase, krow_stride, vrow_stride, kstart, a.L, wave, lane);
+    }
+  } else {
+    st.init(krow_stride, vrow_stride, tid);
+    st.load(kbase, vbase, krow_stride, vrow_stride, kstart, a.L, tid);
+    st.store(smem, tid);
+    wait_all();
+  }
   // D = <dO, O> of this row; each wave half holds 64 of the 128 elements
   float D;
   {
@@ -119,39 +154,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
     for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
     if (lane == 0) a.sink_part[((size_t)head * a.B + b) * a.n_qtiles + p0 / kQT] = t;
   }
-
-  const float c = a.scale_log2;
-  f32x16 acc[kDQK / 32];
-#pragma unroll
-  for (int t = 0; t < kDQK / 32; ++t) acc[t] = zero16();
-
-  const int K0 = max(0, P0 - a.window + 1);
-  const int kstart = (K0 / BK) * BK;
-  const int nblk = (P1 - kstart + BK - 1) / BK;
-
-  // bf16 blocks go global -> LDS directly (no staging registers), fp32 through registers
-  constexpr bool kDMA = E::kBytes == 2;
-  KVStager<E, NT, BK, kRopeNone, kVRows> st;
-  KVStagerDMA<NW, BK, kVRows> dma;
-  if constexpr (kDMA) {
-    dma.init(krow_stride, vrow_stride, wave, lane);
-    dma.load(smem, kbase, vbase, krow_stride, vrow_stride, kstart, a.L, wave, lane);
-    wait_vm();
-  } else {
-    st.init(krow_stride, vrow_stride, tid);
-    st.load(kbase, vbase, krow_stride, vrow_stride, kstart, a.L, tid);
-    st.store(smem, tid);
-    wait_all();
-  }
+  if constexpr (kDMA) wait_vm();  // this wave's K/V fetches have landed
   __syncthreads();
 
   // One block; MASKED is a compile-time copy, the mask-free one serves blocks that every query of
   // this wave's tile sees in full (see the prefill kernel: waves may differ in the range, all run
   // every block with the same stage loads, stores and barriers).
-  auto block = [&](int ib, auto masked_tag) {
+  auto block = [&](int ib, auto masked_tag, auto all_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr bool ALL = decltype(all_tag)::value;  // every block already in its own stage
     const int key0 = kstart + ib * BK;
-    if (ib + 1 < nblk) {
+    if (!ALL && ib + 1 < nblk) {
       if constexpr (kDMA)
         dma.load(smem + ((ib + 1) & 1) * Tile::kStageBytes, kbase, vbase, krow_stride, vrow_stride, key0 + BK,
                  a.L, wave, lane);
@@ -161,7 +174,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
 
     const bool skip = MASKED && ((key0 > p0 + kQT - 1) || (key0 + BK - 1 < p0 - a.window + 1) || (p0 >= a.L));
     if (!skip) {
-      const char* sk = smem + (ib & 1) * Tile::kStageBytes;
+      const char* sk = smem + (ALL ? ib : (ib & 1)) * Tile::kStageBytes;
       const char* sv = sk + Tile::kKBytes;
 
       f32x16 s[NSB], dp[NSB];
@@ -201,12 +214,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
       }
     }
 
-    if constexpr (kDMA) {
-      wait_vm();  // this wave's loads of the next stage have landed
-    } else {
-      if (ib + 1 < nblk) st.store(smem + ((ib + 1) & 1) * Tile::kStageBytes, tid);
+    if constexpr (!ALL) {
+      if constexpr (kDMA) {
+        wait_vm();  // this wave's loads of the next stage have landed
+      } else {
+        if (ib + 1 < nblk) st.store(smem + ((ib + 1) & 1) * Tile::kStageBytes, tid);
+      }
+      __syncthreads();
     }
-    __syncthreads();
   };
 
   // blocks [ib_a, ib_b): every key at or before the tile's first row and within the window of
@@ -222,10 +237,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
   }
   ib_a = __builtin_amdgcn_readfirstlane(ib_a);
   ib_b = __builtin_amdgcn_readfirstlane(ib_b);
-  for (int ib = 0; ib < nblk;) {
-    const int stop = ib < ib_a ? ib_a : (ib < ib_b ? ib : nblk);
-    for (; ib < stop; ++ib) block(ib, std::true_type{});
-    for (; ib < ib_b; ++ib) block(ib, std::false_type{});
+  if (all_blocks) {
+    for (int ib = 0; ib < nblk;) {
+      const int stop = ib < ib_a ? ib_a : (ib < ib_b ? ib : nblk);
+      for (; ib < stop; ++ib) block(ib, std::true_type{}, std::true_type{});
+      for (; ib < ib_b; ++ib) block(ib, std::false_type{}, std::true_type{});
+    }
+  } else {
+    for (int ib = 0; ib < nblk;) {
+      const int stop = ib < ib_a ? ib_a : (ib < ib_b ? ib : nblk);
+      for (; ib < stop; ++ib) block(ib, std::true_type{}, std::false_type{});
+      for (; ib < ib_b; ++ib) block(ib, std::false_type{}, std::false_type{});
+    }
   }
 
   char* dqrow = (char*)a.dq + row * kDQK * E::kBytes;
