@@ -28,6 +28,7 @@ import json
 import math
 import os
 import sys
+import statistics
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -143,7 +144,9 @@ class Case:
 
     def time(self, steps, warmup, min_warm_s=0.25):
         """W untimed warm-up steps (continued until min_warm_s has passed, so clocks have
-        settled), then exactly `steps` timed steps."""
+        settled), then exactly `steps` timed steps. Returns the mean wall-clock and HIP-event time
+        per step; the per-step event times (an event between consecutive steps, on the launch
+        stream) are kept in self.step_ms for their median and minimum."""
         import torch
 
         t0 = time.perf_counter()
@@ -154,15 +157,16 @@ class Case:
             if n % 8 == 0:
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
-        ev0.record()
-        for _ in range(steps):
+        evs[0].record()
+        for k in range(steps):
             self.run()
-        ev1.record()
+            evs[k + 1].record()
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-        event_ms = ev0.elapsed_time(ev1) / steps
+        event_ms = evs[0].elapsed_time(evs[-1]) / steps
+        self.step_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(steps))
         return wall_ms, event_ms
 
     def sampled_parity(self, n_rows=8):
@@ -451,8 +455,10 @@ def describe(case, wall_ms, event_ms):
     w = case.w
     tflops = case.flops / (wall_ms * 1e-3) / 1e12
     gbs = case.bytes / (event_ms * 1e-3) / 1e9
+    steps = getattr(case, "step_ms", None) or [event_ms]
     return {
         "workload": w.name, "ms_per_step": round(wall_ms, 4), "kernel_ms": round(event_ms, 4),
+        "kernel_ms_median": round(statistics.median(steps), 4), "kernel_ms_min": round(steps[0], 4),
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[w.dtype], 4),
         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "algorithmic_flop": case.flops, "algorithmic_bytes": case.bytes,
@@ -570,6 +576,8 @@ def main():
                    "window": w.window, "parallelism": "single GPU"},
         "mfma_frac": head["mfma_frac"],
         "hbm_frac": head["hbm_frac"],
+        "kernel_ms_median": head["kernel_ms_median"],
+        "kernel_ms_min": head["kernel_ms_min"],
         "roofline": roofline,
         "cpu_baseline": cpu.get(w.name),
         "parity": parity,
