@@ -624,7 +624,9 @@ struct WindowLds {
   static constexpr int kXBytes = (kDecNW + 2 * kDecNW + kDecNW) * kX;
   static constexpr int kBytes = kQBytes + kNewBytes + kWork + kXBytes;
   static constexpr int kPBytes = kDecNW * 2 * NCB * 64 * 16;  // P fragments over the Q^T rows
-  static_assert(kPBytes + 4 * kDDV * 2 <= kQBytes, "P fragments and tokens 4..7's V rows fit the Q^T rows");
+  // the new tokens' V rows as a 16-row tile (rows past T zero) beside the P fragments
+  static constexpr int kNewVBytes = 16 * L::kVStride * 2;
+  static_assert(kPBytes + kNewVBytes <= kQBytes, "P fragments and the new tokens' V tile fit the Q^T rows");
 };
 
 template <int NCB, bool ROPE, bool EXT>
@@ -818,10 +820,21 @@ void decode_window_kernel(const DecodeArgs a) {
       st16(sp + (((wave * 2 + ks) * NCB + cb) * 64 + lane) * 16, __builtin_bit_cast(u32x4, frag_from_acc<E>(s[cb], 8 * ks)));
     if (half == 0) xl[(wave * NCB + cb) * 32 + col] = rs;
   }
-  // V rows of tokens 4..7 next to the P fragments, in the part of the Q^T rows P leaves free
-  char* snew_hi = sq + W::kPBytes;
-  if (EXT && tid < nvx) st16(snew_hi + tid * 16, vx);
-  __syncthreads();  // P fragments, block sums and the V rows of tokens 4..7 are in LDS
+  // the new tokens' V rows as one 16-row tile next to the P fragments, in the part of the Q^T
+  // rows P leaves free (padded rows like the V tiles, rows T..15 zero): they enter O^T through one
+  // more MFMA per column block. Rows 0..3 come from the staged new tokens, rows 4..7 (EXT) from
+  // the chunks fetched into registers at the start.
+  char* vnew = sq + W::kPBytes;
+  {
+    constexpr int kCh = kDDV / E::kPerChunk;  // 16-byte chunks per V row
+    const int r = tid / kCh, ch = tid % kCh;  // 256 threads: rows 0..15
+    if (r < 4 || r >= a.T || !EXT) {
+      const u32x4 x = r < a.T && r < 4 ? ld16(snew + Lds::kNewKBytes + r * kDDV * E::kBytes + ch * 16) : zero_chunk();
+      st16(vnew + (r * Lds::kVStride) * E::kBytes + ch * 16, x);
+    }
+    if (EXT && tid < nvx) st16(vnew + ((4 + tid / kCh) * Lds::kVStride) * E::kBytes + (tid % kCh) * 16, vx);
+  }
+  __syncthreads();  // P fragments, block sums and the new tokens' V tile are in LDS
 
   // ---- 3. dv rows 32 wave .. 32 wave + 31 of O^T over all blocks, new tokens, sink ----
   f32x16 acc[NCB];
@@ -844,20 +857,21 @@ void decode_window_kernel(const DecodeArgs a) {
     float L = a.sink && cvalid[cb] ? fast_exp2(sink_l2[cb] - M_use) : 0.f;
 #pragma unroll
     for (int w = 0; w < kDecNW; ++w) L += xl[(w * NCB + cb) * 32 + col];
+    // new tokens: p of token t for this lane's column; the B fragment of one 16-key MFMA step
+    // holds, in lane half h, tokens 4h .. 4h + 3 then four zeros (the key order of the
+    // transposing V^T read: keys 4h..4h+3, then 8+4h..8+4h+3, rows 8..15 of the tile being zero)
+    auto pnew = [&](int t) { return t < kNT && t < a.T ? fast_exp2(snt[t < kNT ? t : 0][cb] - M_use) : 0.f; };
+    {
+      float f[8];
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
-      if (t >= a.T) break;
-      const float pn = fast_exp2(snt[t][cb] - M_use);
-      L += pn;
-      const char* vrow = t < 4 ? snew + Lds::kNewKBytes + t * kDDV * E::kBytes : snew_hi + (t - 4) * kDDV * E::kBytes;
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const u32x2 w2 = *reinterpret_cast<const u32x2*>(vrow + (32 * wave + 8 * gq + 4 * half) * 2);
-        acc[cb][4 * gq + 0] = __builtin_fmaf(pn, __uint_as_float(w2[0] << 16), acc[cb][4 * gq + 0]);
-        acc[cb][4 * gq + 1] = __builtin_fmaf(pn, __uint_as_float(w2[0] & 0xFFFF0000u), acc[cb][4 * gq + 1]);
-        acc[cb][4 * gq + 2] = __builtin_fmaf(pn, __uint_as_float(w2[1] << 16), acc[cb][4 * gq + 2]);
-        acc[cb][4 * gq + 3] = __builtin_fmaf(pn, __uint_as_float(w2[1] & 0xFFFF0000u), acc[cb][4 * gq + 3]);
+      for (int e = 0; e < 4; ++e) {
+        const float lo = pnew(e), hi = pnew(4 + e);  // scalars: a select of two array elements
+        L += lo + hi;                                // became a run-time index into memory
+        f[e] = half ? hi : lo;
+        f[4 + e] = 0.f;
       }
+      const bf16x8 pf = frag_from_f32<E>(f);
+      acc[cb] = mma(vt_frag_tr(vnew, Lds::kVStride, wave, 0, lane), pf, acc[cb]);
     }
     if (!cvalid[cb]) continue;
     const float inv = 1.f / L;
