@@ -768,26 +768,39 @@ void decode_window_kernel(const DecodeArgs a) {
   }
   // score of new token t for this lane's column of every column block: q . k over this half's 96
   // elements (K chunks from `krow` in LDS, or from registers for tokens 4..7), then across halves
-  auto new_score = [&](int t, const char* krow, bool in_regs) {
+  // (EXT: tokens wave and wave + 4 in one pass, sharing the Q^T chunk reads)
+  auto new_scores = [&](const char* krow) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const char* qrow = sq + (cb * 32 + col) * Lds::kQStride * E::kBytes;
-      float dot = 0.f;
+      float dot = 0.f, dot_hi = 0.f;
 #pragma unroll
       for (int i = 0; i < kHalfChunks; ++i) {
         const int e0 = (kDDQK / 2) * half + E::kPerChunk * i;
         const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + e0 * E::kBytes);
-        const u32x4 kv = in_regs ? kx[EXT ? i : 0] : *reinterpret_cast<const u32x4*>(krow + e0 * E::kBytes);
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + e0 * E::kBytes);
 #pragma unroll
         for (int j = 0; j < 4; ++j) dot = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[j]), as_bf16x2(kv[j]), dot, false);
+        if constexpr (EXT) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            dot_hi = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[j]), as_bf16x2(kx[i][j]), dot_hi, false);
+        }
       }
       dot = halves_sum(dot);
+      const int t = wave;
       const bool vis = cvalid[cb] && tq[cb] >= t && tq[cb] - t < a.window;
-      if (half == 0) xs[(t * NCB + cb) * 32 + col] = vis ? dot * c : -INFINITY;
+      if (half == 0 && t < a.T) xs[(t * NCB + cb) * 32 + col] = vis ? dot * c : -INFINITY;
+      if constexpr (EXT) {
+        dot_hi = halves_sum(dot_hi);
+        const int th = tok_hi;
+        const bool vis_hi = cvalid[cb] && tq[cb] >= th && tq[cb] - th < a.window;
+        if (half == 0 && th < a.T) xs[(th * NCB + cb) * 32 + col] = vis_hi ? dot_hi * c : -INFINITY;
+      }
     }
   };
-  if (wave < a.T) new_score(wave, snew + wave * kDDQK * E::kBytes, false);
-  if (EXT && tok_hi < a.T) new_score(tok_hi, nullptr, true);
+  // token `wave`'s K row (a clamped, valid row when wave >= T; its score is then not written)
+  if (wave < a.T || EXT) new_scores(snew + min(wave, a.T - 1) * kDDQK * E::kBytes);
   __syncthreads();  // maxima and new-token scores are in LDS; Q^T is no longer read
 
   // ---- 2. P of this block against the common maximum ----
