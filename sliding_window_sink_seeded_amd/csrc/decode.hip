@@ -189,8 +189,9 @@ struct QStage {
     }
   }
 
-  // Q^T rows at smem, new tokens 0..3 (K rows, then V rows) right after them; the new tokens only
-  // when `last` (the split that folds them in)
+  // Q^T rows at smem, new tokens 0..3 (K rows, then V rows unless !STAGE_V) right after them; the
+  // new tokens only when `last` (the split that folds them in)
+  template <bool STAGE_V = true>
   __device__ __forceinline__ void store(char* smem, int tid, int ncols, bool last, int T) const {
     const int lane = tid & 63;
     u32x4 x[kQPer];
@@ -223,10 +224,19 @@ struct QStage {
       if (last && u < 4 * (kKCh + kVCh) && t < T) {
         if (ch < kKCh)
           st16(snew + t * kDDQK * E::kBytes + ch * 16, x);
-        else
+        else if (STAGE_V)
           st16(snew + Lds::kNewKBytes + t * kDDV * E::kBytes + (ch - kKCh) * 16, x);
       }
     }
+  }
+  // !STAGE_V: the V chunk this thread holds (new token t_out, chunk ch_out of its V row), if any
+  __device__ __forceinline__ bool new_v_chunk(int tid, int T, u32x4& x, int& t_out, int& ch_out) const {
+    static_assert(kNewPer == 1, "one new-token chunk per thread");
+    const int t = tid / (kKCh + kVCh), ch = tid % (kKCh + kVCh);
+    x = xn[0];
+    t_out = t;
+    ch_out = ch - kKCh;
+    return tid < 4 * (kKCh + kVCh) && t < T && ch >= kKCh;
   }
 };
 
@@ -617,7 +627,10 @@ __attribute__((amdgpu_waves_per_eu(NCB == 1 && E::kBytes == 2 ? 2 : 1))) void de
 template <int NCB>
 struct WindowLds {
   using L = DecodeLds<BF16, NCB>;
-  static constexpr int kQBytes = L::kQBytes, kNewBytes = L::kNewBytes, kVBytes = L::kVBytes;
+  // new tokens 0..3: K rows only (their V rows stay in the registers they were fetched into until
+  // the 16-row V tile is built; the 1 KB saved keeps the one-column-block instance at 52 KB, which
+  // with LDS allocated in 2 KB granules is three workgroups per CU instead of two)
+  static constexpr int kQBytes = L::kQBytes, kNewBytes = L::kNewKBytes, kVBytes = L::kVBytes;
   static constexpr int kWork = kDecNW * kVBytes;  // the four waves' V tiles
   static constexpr int kX = NCB * 32 * 4;         // one [column block][column] fp32 row
   // exchange: column maxima [wave][cb][col], new-token scores [token][cb][col], sums [wave][cb][col]
@@ -699,6 +712,9 @@ void decode_window_kernel(const DecodeArgs a) {
   }
 
   KeyRows<E> cur;
+  u32x4 vn;  // a chunk of the V row of new token vn_t (< 4) that this thread fetched, if has_vn
+  int vn_t, vn_ch;
+  bool has_vn;
   {
     QStage<E, NCB, ROPE> st;
     st.load(a, tid, b, g, cbase, ncols, P);
@@ -714,7 +730,8 @@ void decode_window_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < KeyRows<E>::kVChunks; ++i) cur.v[i] = zero_chunk();
     }
-    st.store(smem, tid, ncols, true, a.T);
+    st.template store<false>(smem, tid, ncols, true, a.T);
+    has_vn = st.new_v_chunk(tid, a.T, vn, vn_t, vn_ch);
   }
   char* sq = smem;
   char* snew = smem + W::kQBytes;
@@ -835,16 +852,15 @@ void decode_window_kernel(const DecodeArgs a) {
   }
   // the new tokens' V rows as one 16-row tile next to the P fragments, in the part of the Q^T
   // rows P leaves free (padded rows like the V tiles, rows T..15 zero): they enter O^T through one
-  // more MFMA per column block. Rows 0..3 come from the staged new tokens, rows 4..7 (EXT) from
-  // the chunks fetched into registers at the start.
+  // more MFMA per column block. Rows 0..3 come from the chunks fetched with Q at kernel start,
+  // rows 4..7 (EXT) from those fetched with the K rows of tokens 4..7; every chunk of rows 0..T-1
+  // has exactly one holder.
   char* vnew = sq + W::kPBytes;
   {
     constexpr int kCh = kDDV / E::kPerChunk;  // 16-byte chunks per V row
     const int r = tid / kCh, ch = tid % kCh;  // 256 threads: rows 0..15
-    if (r < 4 || r >= a.T || !EXT) {
-      const u32x4 x = r < a.T && r < 4 ? ld16(snew + Lds::kNewKBytes + r * kDDV * E::kBytes + ch * 16) : zero_chunk();
-      st16(vnew + (r * Lds::kVStride) * E::kBytes + ch * 16, x);
-    }
+    if (r >= a.T) st16(vnew + (r * Lds::kVStride) * E::kBytes + ch * 16, zero_chunk());
+    if (has_vn) st16(vnew + (vn_t * Lds::kVStride) * E::kBytes + vn_ch * 16, vn);
     if (EXT && tid < nvx) st16(vnew + ((4 + tid / kCh) * Lds::kVStride) * E::kBytes + (tid % kCh) * 16, vx);
   }
   __syncthreads();  // P fragments, block sums and the new tokens' V tile are in LDS
