@@ -169,6 +169,38 @@ class Case:
         self.step_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(steps))
         return wall_ms, event_ms
 
+    def time_back_to_back(self, steps):
+        """GPU time per step with the host out of the way: `steps` steps are queued behind device
+        copies (256 MB each, keeping the GPU and its memory busy) that outlast their enqueueing,
+        so the GPU runs them back to back; the events bracket the steps only. Short kernels
+        launched one call at a time from Python otherwise leave launch gaps inside the per-step
+        event times. Returns None when the copies could not be made to outlast the enqueueing."""
+        import torch
+
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        n_copies = 8
+        try:
+            for _ in range(3):
+                torch.cuda.synchronize()
+                ev_busy, ev0, ev1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                ev_busy.record()
+                for _ in range(n_copies):
+                    dst.copy_(src)
+                ev0.record()
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    self.run()
+                ev1.record()
+                host_ms = (time.perf_counter() - t0) * 1e3
+                torch.cuda.synchronize()
+                if ev_busy.elapsed_time(ev0) > 1.25 * host_ms:
+                    return ev0.elapsed_time(ev1) / steps
+                n_copies *= 4
+            return None
+        finally:
+            del src, dst
+
     def sampled_parity(self, n_rows=8):
         """Compare a few output rows (all heads) with the oracle; returns error metrics."""
         import numpy as np
@@ -451,12 +483,12 @@ def measured_traffic(workload, kind):
         return None
 
 
-def describe(case, wall_ms, event_ms):
+def describe(case, wall_ms, event_ms, b2b_ms=None):
     w = case.w
     tflops = case.flops / (wall_ms * 1e-3) / 1e12
     gbs = case.bytes / (event_ms * 1e-3) / 1e9
     steps = getattr(case, "step_ms", None) or [event_ms]
-    return {
+    d = {
         "workload": w.name, "ms_per_step": round(wall_ms, 4), "kernel_ms": round(event_ms, 4),
         "kernel_ms_median": round(statistics.median(steps), 4), "kernel_ms_min": round(steps[0], 4),
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[w.dtype], 4),
@@ -464,6 +496,12 @@ def describe(case, wall_ms, event_ms):
         "algorithmic_flop": case.flops, "algorithmic_bytes": case.bytes,
         "rotated_input_sets": case.n_sets,
     }
+    if b2b_ms:
+        # the same steps run back to back on the GPU (no host launch gaps)
+        d["kernel_ms_back_to_back"] = round(b2b_ms, 4)
+        d["hbm_frac_back_to_back"] = round(case.bytes / (b2b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        d["mfma_frac_back_to_back"] = round(case.flops / (b2b_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4)
+    return d
 
 
 def main():
@@ -545,7 +583,8 @@ def main():
         for name in names[1:]:
             c = Case(workloads.WORKLOADS[name])
             sw, se = c.time(max(5, args.steps // 2), 3, args.warm_seconds)
-            d = describe(c, sw, se)
+            b2b = c.time_back_to_back(max(5, args.steps // 2))
+            d = describe(c, sw, se, b2b)
             d["cpu_baseline"] = cpu.get(name)
             log(f"[bench] {name}: {d}")
             secondary.append(d)
