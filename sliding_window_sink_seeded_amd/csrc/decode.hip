@@ -1003,9 +1003,13 @@ __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2)
   P = P < 0 ? 0 : (P > a.max_len ? a.max_len : P);
   const int off = a.cache_offset ? a.cache_offset[b] : 0;
   const int list0 = max(0, P - a.window + 1);
-  const int s0 = list0 + split * a.keys_per_split;
-  const int s1 = min(P, s0 + a.keys_per_split);
-  const int nb = s1 > s0 ? (s1 - s0 + 31) / 32 : 0;
+  // split s takes the 32-key blocks s, s + nsplit, s + 2 nsplit, ... of the keys [list0, P): the
+  // splits of a sequence then read neighbouring blocks at the same time instead of each streaming
+  // its own contiguous stretch (long-context decode 0.929 -> 0.918 ms)
+  const int s1 = P;
+  const int nbt = P > list0 ? (P - list0 + 31) / 32 : 0;
+  const int nb = split < nbt ? (nbt - 1 - split) / a.nsplit + 1 : 0;
+  auto bkey = [&](int i) { return list0 + 32 * (i * a.nsplit + split); };
 
   const size_t krow_bytes = (size_t)kDDQK * 2, vrow_bytes = (size_t)kDDV * 2;
   const char* kc = (const char*)a.k_cache + (size_t)g * krow_bytes;
@@ -1025,8 +1029,8 @@ __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2)
 
   // the first two blocks' requests, then the Q^T fragments (rotated at position P + t with RoPE)
   ColsRegs r0, r1;
-  if (nb > 0) cols_load(r0, kc, vc, kstride, vstride, row0, s0, s1, off, a.C, tid);
-  if (nb > 1) cols_load(r1, kc, vc, kstride, vstride, row0, s0 + 32, s1, off, a.C, tid);
+  if (nb > 0) cols_load(r0, kc, vc, kstride, vstride, row0, bkey(0), s1, off, a.C, tid);
+  if (nb > 1) cols_load(r1, kc, vc, kstride, vstride, row0, bkey(1), s1, off, a.C, tid);
   bf16x8 qf[kDDQK / 16];
   {
     const char* qrow = (const char*)a.q + (((size_t)b * a.T + t) * a.Hq + head) * krow_bytes;
@@ -1101,9 +1105,9 @@ __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2)
   // block i's math, writes block i + 1 into the other stage (free: read in step i - 1) and closes
   // with a barrier; the register sets and stages alternate, so the loop runs two steps per trip
   auto step = [&](int i, const char* cur, char* other, ColsRegs& mine, const ColsRegs& next) {
-    if (i + 2 < nb) cols_load(mine, kc, vc, kstride, vstride, row0, s0 + 32 * (i + 2), s1, off, a.C, tid);
+    if (i + 2 < nb) cols_load(mine, kc, vc, kstride, vstride, row0, bkey(i + 2), s1, off, a.C, tid);
     __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the math
-    const int key0 = s0 + 32 * i;
+    const int key0 = bkey(i);
     const bool full = key0 + 32 <= s1 && P + a.T - 1 - key0 < a.window;
     block(cur, full, [&](int k) { return key0 + k < s1 && qpos - (key0 + k) < a.window; });
     if (i + 1 < nb) cols_store(other, next, tid);
