@@ -53,7 +53,7 @@ struct DecodeLds {
   static constexpr int kMergeBytes = kDecNW * 2 * 16 * 64 * 4;  // two dv blocks of one column block
   static constexpr int kWorkBytes = kDecNW * kVBytes > kMergeBytes ? kDecNW * kVBytes : kMergeBytes;
   // K and V rows of new tokens 0..3, staged with Q at kernel start (tokens 4..7 of a block draft
-  // go to the work area after the key loop, which keeps the ring kernel at three workgroups per CU)
+  // go to the work area after the key loop rather than growing this area)
   static constexpr int kNewKBytes = 4 * kDDQK * E::kBytes;
   static constexpr int kNewBytes = kNewKBytes + 4 * kDDV * E::kBytes;
   static_assert(4 * (kDDQK + kDDV) * E::kBytes <= kDecNW * kVBytes, "tokens 4..7 fit the V tiles");
