@@ -106,7 +106,9 @@ size_t mimo_attn_decode_workspace_size(int B, int T, int Hq, int Hkv, int d_v, i
  *   tokens 0..t. The caller appends accepted tokens to the cache afterwards.
  *   o   [B, T, Hq, d_v] dtype dt (written);  lse [B, T, Hq] fp32, nullable.
  *   num_splits: 0 = automatic; 1 = single pass per (sequence, KV head); > 1 = split the visible keys
- *   into that many chunks (partials in `workspace`) followed by a combine that adds the sink once.
+ *   into that many parts (partials in `workspace`) followed by a combine that adds the sink once.
+ *   A part is a contiguous stretch of keys, or, for bf16 calls with more than 32 query columns per
+ *   KV head, every num_splits-th block of 32 keys; either way each key enters exactly one part.
  *   workspace / workspace_bytes: device scratch of at least mimo_attn_decode_workspace_size(...)
  *   bytes (may be NULL when that size is 0). Its contents are overwritten.
  *
