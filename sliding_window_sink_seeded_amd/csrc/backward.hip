@@ -255,6 +255,192 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
   store_out_row<E>(dqrow, acc, a.scale, half, valid);
 }
 
+// ------------------------------------------------------------ sliding-window dQ: ping-pong walk
+
+// bf16, window <= 129, eight query heads per workgroup (wave w = head w of the chunk). The dQ
+// kernel's math on a walk over a segment of consecutive 32-row tiles of one (b, g, head chunk):
+// the window of tile t is the 32-key blocks t - 4 .. t, held in an LDS ring (block kb in slot
+// kb mod kDqRing), so each K/V row is fetched once per segment. The two halves of the workgroup
+// run one phase apart: waves 0-3 take tile t's rows (Q, dO and O: D, the sink partial) and fetch
+// K/V block t into the ring while waves 4-7 compute tile t - 1, then waves 0-3 compute tile t
+// while waves 4-7 take tile t's rows; a barrier closes every phase. Each SIMD holds one wave of
+// each half, so one of its waves computes while the other waits for memory, and the rows of half
+// the heads are always in flight. (The one-tile-per-workgroup kernel above runs one workgroup per
+// compute unit, which loads and then computes: per-workgroup timestamps on the 4 x 32768 sliding
+// window layer showed 13.6 us of waiting for rows and K/V blocks, then 6.5 us of products and 2 us
+// of stores, with most compute units in the same phase at once.)
+// Ring slots: tile t's rows phase (waves 0-3) overwrites the slot of block t - 6, last read by
+// waves 4-7 when they computed tile t - 2, two phases earlier.
+constexpr int kDqRing = 6;
+
+// SHORT: windows shorter than 128 keys, where the middle blocks of a window are masked as well
+template <bool SHORT>
+__global__ __launch_bounds__(512) void bwd_dq_swa_kernel(const BackwardArgs a) {
+  using E = BF16;
+  using Tile = PrefillTile<E, 32, kVRows>;
+  using Frag = bf16x8;
+  __shared__ __attribute__((aligned(16))) char smem[kDqRing * Tile::kStageBytes];
+  poison_lds(smem, sizeof(smem));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: takes tile t's rows while 1 computes tile t - 1
+  const int gw = wave & 3;
+
+  // workgroup -> (segment, head chunk, KV head, sequence); segments of one (b, g) are adjacent
+  int rest = blockIdx.x;
+  const int seg = rest % a.n_segments;
+  rest /= a.n_segments;
+  const int hc = rest % a.n_hchunks;
+  rest /= a.n_hchunks;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  const int head = a.hl.at(g * a.G + hc * 8 + wave);
+  const int t0 = seg * a.tiles_per_wg;
+  const int t1 = min(a.n_qtiles, t0 + a.tiles_per_wg);
+
+  const size_t krow_stride = (size_t)a.Hkv * kDQK * 2;
+  const size_t vrow_stride = (size_t)a.Hkv * kDV * 2;
+  const char* kbase = (const char*)a.k + ((size_t)b * a.L * a.Hkv + g) * kDQK * 2;
+  const char* vbase = (const char*)a.v + ((size_t)b * a.L * a.Hkv + g) * kDV * 2;
+  const float c = a.scale_log2;
+  const int W = a.window;
+  // ring slot of block kb (kb >= -4)
+  auto ring = [&](int kb) { return smem + ((kb + kDqRing) % kDqRing) * Tile::kStageBytes; };
+
+  // the first tiles of a sequence also score the blocks before key 0 (masked): their slots must
+  // hold finite values
+  if (t0 < 4) {
+    for (int i = tid; i < kDqRing * Tile::kStageBytes / 16; i += 512) st16(smem + 16 * i, zero_chunk());
+    __syncthreads();
+  }
+  // waves 0-3 stage the K/V blocks: first the window of tile t0 before its diagonal block
+  // (the stager's per-lane offsets are recomputed for every block from an opaque copy of the lane
+  // index: held across the walk, they took registers the compute phase needs)
+  auto stage = [&](int kb) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    KVStagerDMA<4, 32, kVRows> dma;
+    dma.init(krow_stride, vrow_stride, gw, ln);
+    dma.load(ring(kb), kbase, vbase, krow_stride, vrow_stride, 32 * kb, a.L, gw, ln);
+  };
+  if (grp == 0)
+    for (int kb = max(0, t0 - 4); kb < t0; ++kb) stage(kb);
+
+  // rows phase of tile t: Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T), D of
+  // the rows, their share of the sink gradient; waves 0-3 also fetch K/V block t. Ends when every
+  // load of this wave has landed.
+  Frag qf[kDQK / 16], df[kDV / 16];
+  float D = 0.f, lse2 = 0.f;
+  auto rows = [&](int t) __attribute__((always_inline)) {
+    if (grp == 0) stage(t);
+    const int qpos = kQT * t + col;
+    const bool valid = qpos < a.L;
+    const size_t row = ((size_t)b * a.L + min(qpos, a.L - 1)) * a.Hq + head;
+    const char* qrow = (const char*)a.q + row * kDQK * 2;
+    const char* drow = (const char*)a.d_o + row * kDV * 2;
+    const char* orow = (const char*)a.o + row * kDV * 2;
+#pragma unroll
+    for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
+#pragma unroll
+    for (int kk = 0; kk < kDV / 16; ++kk) df[kk] = global_q_frag<E>(drow, kk, half);
+    float part = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < kDV / 16; ++kk) {
+      float x[8], y[8];
+      frag_to_f32<E>(df[kk], x);
+      frag_to_f32<E>(global_q_frag<E>(orow, kk, half), y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = __builtin_fmaf(x[e], y[e], part);
+    }
+    D = halves_sum(part);
+    const size_t lrow = ((size_t)b * a.Hq + head) * a.L + min(qpos, a.L - 1);
+    lse2 = a.lse[lrow] * kLog2e;
+    if (half == 0 && valid) a.D[lrow] = D;
+    if (a.sink_part) {
+      // this tile's share of d s_h: -sum_i exp(s_h - lse_i) D_i (the sign is applied at the end)
+      float sp = (half == 0 && valid) ? fast_exp2(a.sink[head] * kLog2e - lse2) * D : 0.f;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sp += __shfl_xor(sp, off);
+      if (lane == 0) a.sink_part[((size_t)head * a.B + b) * a.n_qtiles + t] = sp;
+    }
+    wait_vm();
+  };
+
+  // (the phases are forced inline: called from two runs, the compiler made them functions with a
+  // stack frame)
+  // compute phase of tile t: blocks t - 4 .. t. The first and the last are masked; the middle
+  // ones too (ALL) for the first tiles of a sequence (blocks before key 0) and short windows. The
+  // choice is made per run of tiles: inside a tile, a branch between masked and mask-free copies
+  // made the compiler spill the accumulators.
+  auto compute = [&](int t, auto all_tag) __attribute__((always_inline)) {
+    constexpr bool ALL = decltype(all_tag)::value;
+    const int qpos = kQT * t + col;
+    f32x16 acc[kDQK / 32];
+#pragma unroll
+    for (int i = 0; i < kDQK / 32; ++i) acc[i] = zero16();
+    auto block = [&](int kb, auto masked_tag) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      const char* sk = ring(kb);
+      const char* sv = sk + Tile::kKBytes;
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int kk = 0; kk < kDQK / 16; ++kk) s = mma(lds_row_frag<E>(sk, Tile::kKStride, col, kk, half), qf[kk], s);
+#pragma unroll
+      for (int kk = 0; kk < kDV / 16; ++kk) dp = mma(lds_row_frag<E>(sv, Tile::kVStride, col, kk, half), df[kk], dp);
+      // dS^T = P^T (dP^T - D), P^T = exp(S^T * scale - lse), zero where masked (keys before 0
+      // read zeroed slots: finite, and masked here)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+        if constexpr (MASKED) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int d = qpos - key;
+          p = (key >= 0 && d >= 0 && d < W) ? p : 0.f;
+        }
+        s[r] = p * (dp[r] - D);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const Frag dsf = frag_from_acc<E>(s, 8 * ks);
+#pragma unroll
+        for (int i = 0; i < kDQK / 32; ++i) acc[i] = mma(lds_t_frag<E>(sk, Tile::kKStride, i, ks, lane), dsf, acc[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one block at a time
+    };
+    block(t - 4, std::true_type{});
+#pragma unroll
+    for (int j = 1; j < 4; ++j) block(t - 4 + j, std::integral_constant<bool, ALL>{});
+    block(t, std::true_type{});
+    const size_t row = ((size_t)b * a.L + min(qpos, a.L - 1)) * a.Hq + head;
+    store_out_row<E>((char*)a.dq + row * kDQK * 2, acc, a.scale, half, qpos < a.L);
+  };
+
+  auto close_phase = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // tiles [ta, tb): rows phase, then compute phase, each closed by a barrier; waves 4-7 start one
+  // phase late and waves 0-3 end with an idle phase, so both halves pass the same barriers
+  auto run = [&](int ta, int tb, auto all_tag) __attribute__((always_inline)) {
+    for (int t = ta; t < tb; ++t) {
+      rows(t);
+      close_phase();
+      compute(t, all_tag);
+      close_phase();
+    }
+  };
+  if (grp == 1) close_phase();
+  const int tm = SHORT ? t1 : min(t1, max(t0, 4));  // tiles whose window starts before key 0
+  run(t0, tm, std::true_type{});
+  if constexpr (!SHORT) run(tm, t1, std::false_type{});
+  if (grp == 0) close_phase();
+}
+
 // ---------------------------------------------------------------------------------- dK/dV kernel
 
 // LDS stage of one step: Q rows [32][kQS], dO rows [32][kOS], then lse * log2(e) [32] and D [32].
@@ -599,6 +785,11 @@ size_t backward_ws_bytes(int B, int L, int Hq) {
 }
 
 
+// windows the sliding-window dQ walk serves (the window of a 32-row tile is then five 32-key
+// blocks), and its shortest segment
+constexpr int kDqSwaMaxWindow = 129;
+constexpr int kDqSwaMinTiles = 8;
+
 template <typename E>
 static hipError_t launch_backward(BackwardArgs a, hipStream_t stream) {
   // dQ workgroups of 8 waves (bf16) or 4 (fp32: at 8 waves, two per SIMD, its operands need more
@@ -625,7 +816,24 @@ static hipError_t launch_backward(BackwardArgs a, hipStream_t stream) {
   const long long n_dq = (long long)a.n_qblocks * a.B * a.Hkv * a.n_hchunks;
   const long long n_kv = (long long)(a.kv_pairs ? (a.n_kblocks + 1) / 2 : a.n_kblocks) * a.B * a.Hkv;
   if (n_dq > 0x7fffffffLL || n_kv > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_dq_kernel<E, NW, BK>), dim3((unsigned)n_dq), dim3(NW * 64), 0, stream, a);
+  if (E::kBytes == 2 && hg == 8 && a.window <= kDqSwaMaxWindow) {
+    // sliding window: the ping-pong walk over segments of tiles, about one workgroup per compute
+    // unit in total (at least kDqSwaMinTiles tiles per segment, each re-reads a 4-block halo)
+    const long long units = (long long)a.B * a.Hkv * a.n_hchunks;
+    long long segs = (256 + units - 1) / units;
+    long long per = (a.n_qtiles + segs - 1) / segs;
+    if (per < kDqSwaMinTiles) per = kDqSwaMinTiles;
+    a.tiles_per_wg = (int)per;
+    a.n_segments = (int)((a.n_qtiles + per - 1) / per);
+    const long long n_wg = units * a.n_segments;
+    if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (a.window >= 128)
+      hipLaunchKernelGGL(bwd_dq_swa_kernel<false>, dim3((unsigned)n_wg), dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL(bwd_dq_swa_kernel<true>, dim3((unsigned)n_wg), dim3(512), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<E, NW, BK>), dim3((unsigned)n_dq), dim3(NW * 64), 0, stream, a);
+  }
   if constexpr (E::kBytes == 2) {
     if (kv2)
       hipLaunchKernelGGL((bwd_dkdv_kernel<E, 2>), dim3((unsigned)n_kv), dim3(128), 0, stream, a);

@@ -82,6 +82,8 @@ struct BackwardArgs {
   int n_kblocks;        // dk/dv kernel: key blocks per (b, g)
   int kv_pairs;         // dk/dv kernel: 1 = a workgroup takes key blocks p and n_kblocks - 1 - p
   int n_qtiles;         // ceil(L / 32)
+  int n_segments;       // sliding-window dq kernel: segments of consecutive tiles per (b, g, chunk)
+  int tiles_per_wg;     // sliding-window dq kernel: 32-row tiles per segment
   HeadList hl;
 };
 

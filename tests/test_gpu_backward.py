@@ -82,6 +82,26 @@ def test_backward_edge_shapes(dtype, L, W):
     check_all(inp, output_grad(70 + W, 1, L, 8, 128, dtype))
 
 
+# The sliding-window dQ walk (bf16, window <= 129, 8 or 16 query heads per KV head): one KV head
+# and one sequence make the launcher cut the tiles into segments of 8, so these shapes cross
+# several segment boundaries (each segment re-reads a 4-block halo), start segments inside the
+# first four tiles' zeroed blocks, end on ragged tails, and cover the windows whose middle blocks
+# are masked too (W < 128).
+@pytest.mark.parametrize("B,L,Hq,Hkv,W", [
+    (1, 2100, 8, 1, 128),
+    (1, 1000, 16, 1, 129),
+    (2, 777, 8, 1, 127),
+    (1, 300, 8, 2, 64),
+    (1, 40, 8, 1, 1),
+    (1, 1, 8, 1, 128),
+    (1, 97, 8, 1, 128),
+])
+def test_backward_sliding_window_segments(B, L, Hq, Hkv, W):
+    say(f"backward sliding-window walk B={B} L={L} {Hq}/{Hkv} W={W}")
+    inp = prefill_inputs(1000 + L + W, B, L, Hq, Hkv, 192, 128, W, "bf16")
+    check_all(inp, output_grad(1000 + L + W, B, L, Hq, 128, "bf16"))
+
+
 def test_backward_without_sink():
     say("backward no sink")
     inp = prefill_inputs(81, 2, 100, 16, 2, 192, 128, 40, "bf16", with_sink=False)
@@ -166,7 +186,9 @@ def full_size(name, B, L, Hq, Hkv, W, seed, rows, keys):
 
 
 def test_backward_full_size_sliding_window():
-    rows = [(0, 0), (1, 31), (2, 127), (3, 128), (0, 20000), (3, 32767)]
+    # rows 4095 / 4096 and 28671 / 28672 straddle segments of the sliding-window dQ walk
+    rows = [(0, 0), (1, 31), (2, 127), (3, 128), (0, 4095), (0, 4096), (0, 20000), (2, 28671),
+            (2, 28672), (3, 32767)]
     keys = [(0, 0), (1, 100), (2, 128), (3, 5000), (0, 32640), (3, 32767)]
     full_size("swa 4 x 32768, 64/8, W=128", 4, 32768, 64, 8, 128, 91, rows, keys)
 
