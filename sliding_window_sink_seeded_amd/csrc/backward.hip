@@ -262,15 +262,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BackwardArgs a) {
 // the window of tile t is the 32-key blocks t - 4 .. t, held in an LDS ring (block kb in slot
 // kb mod kDqRing), so each K/V row is fetched once per segment. The two halves of the workgroup
 // run one phase apart: waves 0-3 take tile t's rows (Q, dO and O: D, the sink partial) and fetch
-// K/V block t into the ring while waves 4-7 compute tile t - 1, then waves 0-3 compute tile t
-// while waves 4-7 take tile t's rows; a barrier closes every phase. Each SIMD holds one wave of
+// K of block t into the ring while waves 4-7 compute tile t - 1, then waves 0-3 compute tile t
+// while waves 4-7 take tile t's rows and fetch V of block t + 1; a barrier closes every phase. Each SIMD holds one wave of
 // each half, so one of its waves computes while the other waits for memory, and the rows of half
 // the heads are always in flight. (The one-tile-per-workgroup kernel above runs one workgroup per
 // compute unit, which loads and then computes: per-workgroup timestamps on the 4 x 32768 sliding
 // window layer showed 13.6 us of waiting for rows and K/V blocks, then 6.5 us of products and 2 us
 // of stores, with most compute units in the same phase at once.)
-// Ring slots: tile t's rows phase (waves 0-3) overwrites the slot of block t - 6, last read by
-// waves 4-7 when they computed tile t - 2, two phases earlier.
+// Ring slots: block t's slot held block t - 6, last read when waves 4-7 computed tile t - 2; V of
+// block t arrives one phase after that (waves 4-7, rows of tile t - 1), K one phase later still
+// (waves 0-3, rows of tile t), and both before waves 0-3 compute tile t.
 constexpr int kDqRing = 6;
 
 // SHORT: windows shorter than 128 keys, where the middle blocks of a window are masked as well
@@ -318,17 +319,36 @@ __global__ __launch_bounds__(512) void bwd_dq_swa_kernel(const BackwardArgs a) {
     __syncthreads();
   }
   // waves 0-3 stage the K/V blocks: first the window of tile t0 before its diagonal block
-  // (the stager's per-lane offsets are recomputed for every block from an opaque copy of the lane
-  // index: held across the walk, they took registers the compute phase needs)
-  auto stage = [&](int kb) __attribute__((always_inline)) {
+  // Staging global -> LDS by one half (four waves): waves 0-3 fetch K of block t in their rows
+  // phase of tile t, waves 4-7 V of block t + 1 in theirs, so both halves' rows phases carry a
+  // share of the ring traffic. (The stagers' per-lane offsets are recomputed for every block from
+  // an opaque copy of the lane index: held across the walk, they took registers the compute phase
+  // needs.)
+  using KDma = RowsDMA<4, 32, Tile::kKStride * 2 / 16, kDQK / 8>;
+  using VDma = RowsDMA<4, 32, Tile::kVStride * 2 / 16, kDV / 8>;
+  static_assert(KDma::kChunks * 16 == Tile::kKBytes && VDma::kChunks * 16 == Tile::kVBytes, "regions tile the stage");
+  auto stage_k = [&](int kb) __attribute__((always_inline)) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    KVStagerDMA<4, 32, kVRows> dma;
-    dma.init(krow_stride, vrow_stride, gw, ln);
-    dma.load(ring(kb), kbase, vbase, krow_stride, vrow_stride, 32 * kb, a.L, gw, ln);
+    uint32_t off[KDma::kPer];
+    KDma::init(off, krow_stride, gw, ln);
+    KDma::load(off, ring(kb), kbase, krow_stride, 32 * kb, a.L, gw, ln);
   };
-  if (grp == 0)
-    for (int kb = max(0, t0 - 4); kb < t0; ++kb) stage(kb);
+  auto stage_v = [&](int kb) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    uint32_t off[VDma::kPer];
+    VDma::init(off, vrow_stride, gw, ln);
+    VDma::load(off, ring(kb) + Tile::kKBytes, vbase, vrow_stride, 32 * kb, a.L, gw, ln);
+  };
+  // before the walk (waves 0-3): the window of tile t0 before its diagonal block, and V of t0
+  if (grp == 0) {
+    for (int kb = max(0, t0 - 4); kb < t0; ++kb) {
+      stage_k(kb);
+      stage_v(kb);
+    }
+    stage_v(t0);
+  }
 
   // rows phase of tile t: Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T), D of
   // the rows, their share of the sink gradient; waves 0-3 also fetch K/V block t. Ends when every
@@ -336,7 +356,10 @@ __global__ __launch_bounds__(512) void bwd_dq_swa_kernel(const BackwardArgs a) {
   Frag qf[kDQK / 16], df[kDV / 16];
   float D = 0.f, lse2 = 0.f;
   auto rows = [&](int t) __attribute__((always_inline)) {
-    if (grp == 0) stage(t);
+    if (grp == 0)
+      stage_k(t);
+    else if (t + 1 < t1)
+      stage_v(t + 1);
     const int qpos = kQT * t + col;
     const bool valid = qpos < a.L;
     const size_t row = ((size_t)b * a.L + min(qpos, a.L - 1)) * a.Hq + head;
