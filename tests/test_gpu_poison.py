@@ -84,7 +84,8 @@ def test_poisoned_rope():
 
 
 @pytest.mark.parametrize("dtype,B,L,Hq,Hkv,W", [
-    ("bf16", 2, 300, 64, 8, 128),     # two-wave dK/dV workgroups
+    ("bf16", 2, 300, 64, 8, 128),     # two-wave dK/dV workgroups; the sliding-window dQ walk
+    ("bf16", 1, 700, 8, 1, 64),       # the dQ walk with every block masked, three segments
     ("bf16", 1, 297, 16, 2, 10**9),   # paired key blocks
     ("f32", 1, 150, 8, 1, 10**9),
 ])
