@@ -356,32 +356,39 @@ __global__ __launch_bounds__(512) void bwd_dq_swa_kernel(const BackwardArgs a) {
   Frag qf[kDQK / 16], df[kDV / 16];
   float D = 0.f, lse2 = 0.f;
   auto rows = [&](int t) __attribute__((always_inline)) {
-    if (grp == 0)
-      stage_k(t);
-    else if (t + 1 < t1)
-      stage_v(t + 1);
     const int qpos = kQT * t + col;
     const bool valid = qpos < a.L;
     const size_t row = ((size_t)b * a.L + min(qpos, a.L - 1)) * a.Hq + head;
     const char* qrow = (const char*)a.q + row * kDQK * 2;
     const char* drow = (const char*)a.d_o + row * kDV * 2;
     const char* orow = (const char*)a.o + row * kDV * 2;
-#pragma unroll
-    for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
+    const size_t lrow = ((size_t)b * a.Hq + head) * a.L + min(qpos, a.L - 1);
+    // dO, O and lse first: D and the sink partial are formed while Q and the ring block arrive
+    // (requested after Q, they held D back until everything had landed: 5.46 -> 5.37 ms)
+    Frag of[kDV / 16];
 #pragma unroll
     for (int kk = 0; kk < kDV / 16; ++kk) df[kk] = global_q_frag<E>(drow, kk, half);
+#pragma unroll
+    for (int kk = 0; kk < kDV / 16; ++kk) of[kk] = global_q_frag<E>(orow, kk, half);
+    lse2 = a.lse[lrow] * kLog2e;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
+    if (grp == 0)
+      stage_k(t);
+    else if (t + 1 < t1)
+      stage_v(t + 1);
+    __builtin_amdgcn_sched_barrier(0);
     float part = 0.f;
 #pragma unroll
     for (int kk = 0; kk < kDV / 16; ++kk) {
       float x[8], y[8];
       frag_to_f32<E>(df[kk], x);
-      frag_to_f32<E>(global_q_frag<E>(orow, kk, half), y);
+      frag_to_f32<E>(of[kk], y);
 #pragma unroll
       for (int e = 0; e < 8; ++e) part = __builtin_fmaf(x[e], y[e], part);
     }
     D = halves_sum(part);
-    const size_t lrow = ((size_t)b * a.Hq + head) * a.L + min(qpos, a.L - 1);
-    lse2 = a.lse[lrow] * kLog2e;
     if (half == 0 && valid) a.D[lrow] = D;
     if (a.sink_part) {
       // this tile's share of d s_h: -sum_i exp(s_h - lse_i) D_i (the sign is applied at the end)
