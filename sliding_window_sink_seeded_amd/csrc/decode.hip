@@ -679,7 +679,6 @@ void decode_window_kernel(const DecodeArgs a) {
   const int s0 = max(0, P - a.window + 1);  // committed keys [s0, P), at most 128
   const int s1 = P;
   const int key0 = s0 + 32 * wave;
-  const bool has_keys = key0 < s1;
 
   const size_t krow_bytes = (size_t)kDDQK * E::kBytes;
   const size_t vrow_bytes = (size_t)kDDV * E::kBytes;
@@ -718,18 +717,17 @@ void decode_window_kernel(const DecodeArgs a) {
   {
     QStage<E, NCB, ROPE> st;
     st.load(a, tid, b, g, cbase, ncols, P);
-    if (has_keys) {
-      const int pos = min(key0 + col, s1 - 1);
-      int slot = (pos + off) % a.C;
-      slot += slot < 0 ? a.C : 0;
-      cur.load((const char*)a.k_cache + ((row0 + slot) * a.Hkv + g) * krow_bytes,
-               (const char*)a.v_cache + ((row0 + slot) * a.Hkv + g) * vrow_bytes, half);
-    } else {
-#pragma unroll
-      for (int j = 0; j < KeyRows<E>::kKChunks; ++j) cur.k[j] = zero_chunk();
-#pragma unroll
-      for (int i = 0; i < KeyRows<E>::kVChunks; ++i) cur.v[i] = zero_chunk();
-    }
+    // Every wave fetches its K and V rows unconditionally, so the compiler can count them in
+    // order behind the Q rows: the Q^T store waits for Q alone and the scores for K alone (with
+    // the fetch inside a branch, every wait before the first barrier covered all of them). A
+    // wave past the committed keys reads the last committed key; with no committed key at all it
+    // reads new token 0 (finite data either way, its scores are masked and P is 0).
+    const int pos = max(min(key0 + col, s1 - 1), 0);
+    int slot = (pos + off) % a.C;
+    slot += slot < 0 ? a.C : 0;
+    const size_t kv_row = s1 > 0 ? (row0 + slot) * a.Hkv + g : (size_t)b * a.T * a.Hkv + g;
+    cur.load((const char*)(s1 > 0 ? a.k_cache : a.k_new) + kv_row * krow_bytes,
+             (const char*)(s1 > 0 ? a.v_cache : a.v_new) + kv_row * vrow_bytes, half);
     st.template store<false>(smem, tid, ncols, true, a.T);
     has_vn = st.new_v_chunk(tid, a.T, vn, vn_t, vn_ch);
   }
@@ -757,7 +755,6 @@ void decode_window_kernel(const DecodeArgs a) {
   const float c = a.scale_log2;
 
   // ---- 1. S^T of this wave's block, column maxima, new tokens `wave` and `wave + 4` ----
-  cur.store_v(work + wave * W::kVBytes, col, half);
   f32x16 s[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) s[cb] = zero16();
@@ -818,6 +815,10 @@ void decode_window_kernel(const DecodeArgs a) {
   };
   // token `wave`'s K row (a clamped, valid row when wave >= T; its score is then not written)
   if (wave < a.T || EXT) new_scores(snew + min(wave, a.T - 1) * kDDQK * E::kBytes);
+  // the V half rows (requested after the K half rows) go to the wave's V tile only now, so the
+  // scores above wait for K alone (stored before them, every MFMA waited for the V rows too)
+  __builtin_amdgcn_sched_barrier(0);
+  cur.store_v(work + wave * W::kVBytes, col, half);
   __syncthreads();  // maxima and new-token scores are in LDS; Q^T is no longer read
 
   // ---- 2. P of this block against the common maximum ----
