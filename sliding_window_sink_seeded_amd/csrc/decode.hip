@@ -183,9 +183,8 @@ struct QStage {
                             : (const char*)a.v_new + (((size_t)b * a.T + t) * a.Hkv + g) * vrow_bytes +
                                   (ch - kKCh) * 16;
       xn[i] = ld16(src);
-      if constexpr (ROPE) {
-        if (ch < 2 * H) rope_load<E::kPerChunk>(a.rope, P + t, (ch % H) * E::kPerChunk, ncs[i]);
-      }
+      // (every lane reads table entries, used only for rotated chunks: no branch around loads)
+      if constexpr (ROPE) rope_load<E::kPerChunk>(a.rope, P + t, (ch % H) * E::kPerChunk, ncs[i]);
     }
   }
 
@@ -701,13 +700,12 @@ void decode_window_kernel(const DecodeArgs a) {
     const char* krow = (const char*)a.k_new + (((size_t)b * a.T + t) * a.Hkv + g) * krow_bytes + half * (kDDQK / 2) * E::kBytes;
 #pragma unroll
     for (int i = 0; i < kHalfChunks; ++i) kx[i] = ld16(krow + 16 * i);
-    if (tid < nvx) {
-      const int tv = 4 + tid / (kDDV / E::kPerChunk), ch = tid % (kDDV / E::kPerChunk);
+    {  // unconditional (threads past nvx re-read a valid chunk, unused), like the K/V rows below
+      const int u = min(tid, nvx - 1);  // nvx >= 16: this instance runs only with T > 4
+      const int tv = 4 + u / (kDDV / E::kPerChunk), ch = u % (kDDV / E::kPerChunk);
       vx = ld16((const char*)a.v_new + (((size_t)b * a.T + tv) * a.Hkv + g) * vrow_bytes + ch * 16);
     }
-    if constexpr (ROPE) {
-      if (half == 0) rope_load<kRopeDims / 2>(a.rope, P + t, 0, xcs);
-    }
+    if constexpr (ROPE) rope_load<kRopeDims / 2>(a.rope, P + t, 0, xcs);  // every lane: no branch
   }
 
   KeyRows<E> cur;
@@ -1029,9 +1027,19 @@ __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2)
   const int qpos = P + t;
 
   // the first two blocks' requests, then the Q^T fragments (rotated at position P + t with RoPE)
+  // With 128 columns every fetch below is unconditional (past the split's last block: that block
+  // again, unused), so the compiler's wait counts see one straight-line sequence and the fetch
+  // of block i + 2 stays in flight across step i. Under branches (as with 64 columns), each
+  // step's LDS store waits for the fetch issued at the top of that same step, and the products
+  // for everything in flight: about one block ahead instead of two. Measured: 128 columns (16
+  // heads x 8 tokens) 1.035 -> 1.010 ms with the two-ahead fetch; 64 columns 0.947 -> 0.983 ms,
+  // so those keep the branches (more fetches in flight from every workgroup read the cache at
+  // more places at once).
+  constexpr bool kAhead2 = NCB == 4;
   ColsRegs r0, r1;
-  if (nb > 0) cols_load(r0, kc, vc, kstride, vstride, row0, bkey(0), s1, off, a.C, tid);
-  if (nb > 1) cols_load(r1, kc, vc, kstride, vstride, row0, bkey(1), s1, off, a.C, tid);
+  if (kAhead2 || nb > 0) cols_load(r0, kc, vc, kstride, vstride, row0, bkey(0), s1, off, a.C, tid);
+  if (kAhead2 || nb > 1)
+    cols_load(r1, kc, vc, kstride, vstride, row0, bkey(min(1, max(nb - 1, 0))), s1, off, a.C, tid);
   bf16x8 qf[kDDQK / 16];
   {
     const char* qrow = (const char*)a.q + (((size_t)b * a.T + t) * a.Hq + head) * krow_bytes;
@@ -1047,6 +1055,7 @@ __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2)
     }
   }
   if (nb > 0) cols_store(st0, r0, tid);
+  if constexpr (kAhead2) wait_all();  // Q^T (fetched last) has landed; the loop counts its own fetches
   __syncthreads();
 
   const float c2 = a.scale_log2;
@@ -1106,7 +1115,8 @@ __global__ __launch_bounds__(kColsNW * 64) __attribute__((amdgpu_waves_per_eu(2)
   // block i's math, writes block i + 1 into the other stage (free: read in step i - 1) and closes
   // with a barrier; the register sets and stages alternate, so the loop runs two steps per trip
   auto step = [&](int i, const char* cur, char* other, ColsRegs& mine, const ColsRegs& next) {
-    if (i + 2 < nb) cols_load(mine, kc, vc, kstride, vstride, row0, bkey(i + 2), s1, off, a.C, tid);
+    if (kAhead2 || i + 2 < nb)
+      cols_load(mine, kc, vc, kstride, vstride, row0, bkey(min(i + 2, nb - 1)), s1, off, a.C, tid);
     __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the math
     const int key0 = bkey(i);
     const bool full = key0 + 32 <= s1 && P + a.T - 1 - key0 < a.window;
