@@ -356,7 +356,13 @@ __global__ __launch_bounds__(512) void bwd_dq_swa_kernel(const BackwardArgs a) {
   Frag qf[kDQK / 16], df[kDV / 16];
   float D = 0.f, lse2 = 0.f;
   auto rows = [&](int t) __attribute__((always_inline)) {
-    const int qpos = kQT * t + col;
+    // the row addresses come from an opaque copy of the lane index: hoisted out of the walk, the
+    // per-lane pointers were spilled and reloaded between the batches of fetches (each reload
+    // waiting for every fetch before it; no change in time measured, 60 -> 36 B of scratch)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lcol = ln & 31, lhalf = ln >> 5;
+    const int qpos = kQT * t + lcol;
     const bool valid = qpos < a.L;
     const size_t row = ((size_t)b * a.L + min(qpos, a.L - 1)) * a.Hq + head;
     const char* qrow = (const char*)a.q + row * kDQK * 2;
@@ -367,13 +373,13 @@ __global__ __launch_bounds__(512) void bwd_dq_swa_kernel(const BackwardArgs a) {
     // (requested after Q, they held D back until everything had landed: 5.46 -> 5.37 ms)
     Frag of[kDV / 16];
 #pragma unroll
-    for (int kk = 0; kk < kDV / 16; ++kk) df[kk] = global_q_frag<E>(drow, kk, half);
+    for (int kk = 0; kk < kDV / 16; ++kk) df[kk] = global_q_frag<E>(drow, kk, lhalf);
 #pragma unroll
-    for (int kk = 0; kk < kDV / 16; ++kk) of[kk] = global_q_frag<E>(orow, kk, half);
+    for (int kk = 0; kk < kDV / 16; ++kk) of[kk] = global_q_frag<E>(orow, kk, lhalf);
     lse2 = a.lse[lrow] * kLog2e;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, half);
+    for (int kk = 0; kk < kDQK / 16; ++kk) qf[kk] = global_q_frag<E>(qrow, kk, lhalf);
     if (grp == 0)
       stage_k(t);
     else if (t + 1 < t1)
@@ -389,10 +395,10 @@ __global__ __launch_bounds__(512) void bwd_dq_swa_kernel(const BackwardArgs a) {
       for (int e = 0; e < 8; ++e) part = __builtin_fmaf(x[e], y[e], part);
     }
     D = halves_sum(part);
-    if (half == 0 && valid) a.D[lrow] = D;
+    if (lhalf == 0 && valid) a.D[lrow] = D;
     if (a.sink_part) {
       // this tile's share of d s_h: -sum_i exp(s_h - lse_i) D_i (the sign is applied at the end)
-      float sp = (half == 0 && valid) ? fast_exp2(a.sink[head] * kLog2e - lse2) * D : 0.f;
+      float sp = (lhalf == 0 && valid) ? fast_exp2(a.sink[head] * kLog2e - lse2) * D : 0.f;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) sp += __shfl_xor(sp, off);
       if (lane == 0) a.sink_part[((size_t)head * a.B + b) * a.n_qtiles + t] = sp;
